@@ -1,0 +1,259 @@
+"""Benchmark: fused causal GQA flash-attention prefill on one MI355X.
+
+Workload (one step): a 16k-token prefill of gpt-oss attention geometry run
+as 32 chunks of 512 tokens over a growing KV cache (chunk c at past_len
+512c), through 24 layers that alternate full attention and a 128-key
+sliding window (12 of each), H_q = 64, H_kv = 8, d = 64, fp16, per-head
+sinks.  Every layer owns its own q / cache / out buffers (so no layer finds
+another's KV in cache), all resident in HBM before timing starts.  Calls run
+chunk-major (chunk c through all 24 layers, then chunk c + 1), as a model's
+chunked prefill does.
+
+Reported: useful TFLOP/s over the whole step (useful = 4 * d * H_q per kept
+(query, key) pair; masked work in visited tiles does not count), the full-
+attention layers' TFLOP/s and fraction of the MI355X dense fp16/bf16 MFMA
+peak, and microseconds per layer call, from HIP events recorded around every
+launch on the launch stream inside the timed region.  Beside it: the CPU
+oracle's throughput on a bounded row sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS_F16 = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill attention useful TFLOP/s & % bf16 MFMA peak; us/layer-call at 16k"
+
+H_Q, H_KV, D, WINDOW = 64, 8, 64, 128
+LAYERS, CHUNK, TOKENS = 24, 512, 16384
+N_CHUNKS = TOKENS // CHUNK
+
+
+def kept_pairs(past, sq, window):
+    """Kept (query, key) pairs of one head for a chunk of sq rows after past keys."""
+    pos = past + np.arange(sq, dtype=np.int64)
+    lo = np.zeros_like(pos) if window <= 0 else np.maximum(0, pos - window + 1)
+    return int((pos - lo + 1).sum())
+
+
+def useful_flops(past, sq, window):
+    return 4.0 * D * H_Q * kept_pairs(past, sq, window)
+
+
+def algorithmic_bytes(past, sq, window, elem=2):
+    """Q read + O write + K and V over the keys the chunk's rows keep (union)."""
+    lo = 0 if window <= 0 else max(0, past - window + 1)
+    keys = past + sq - lo
+    return elem * (2 * sq * H_Q * D + 2 * keys * H_KV * D)
+
+
+def layer_window(layer):
+    return WINDOW if layer % 2 == 1 else -1
+
+
+def make_layers(torch, dev):
+    """Per-layer device buffers, drawn with the seeded generator recipe of
+    gqa_flash_attention_prefill_amd.synth (N(0,1) in fp32 rounded to fp16)."""
+    from gqa_flash_attention_prefill_amd import synth
+    layers = []
+    for layer in range(LAYERS):
+        case = synth.chunked16k_layer(layer)
+        inp = synth.make(case, device=dev)
+        out = torch.empty_like(inp["q"])
+        layers.append((case, inp, out))
+    return layers
+
+
+def cpu_baseline(torch, layers_cpu, budget_s=12.0):
+    """Time the oracle (as it stands) on a row sample of the workload: rows
+    drawn uniformly over the 16k positions and all 64 heads of one full and
+    one window layer (a chunk row equals the same row of one whole-sequence
+    prefill, so the oracle runs on the whole-sequence view).  The sample size
+    is calibrated to about `budget_s` seconds of oracle time."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    rng = np.random.default_rng(1234)
+    prepared = []
+    for case, inp in layers_cpu:
+        prepared.append((case, {
+            "q": inp["q"].double().numpy(), "k": inp["k_cache"].double().numpy(),
+            "v": inp["v_cache"].double().numpy(), "sink": inp["sink"].double().numpy()}))
+
+    def run(n_rows):
+        flops, secs = 0.0, 0.0
+        for case, a in prepared:
+            toks = rng.integers(0, TOKENS, size=n_rows)
+            heads = rng.integers(0, H_Q, size=n_rows).astype(np.int32)
+            lo = np.zeros_like(toks) if case.window <= 0 else np.maximum(0, toks - case.window + 1)
+            flops += 4.0 * D * float((toks - lo + 1).sum())
+            t0 = time.perf_counter()
+            oracle.attn_rows(a["q"], a["k"], a["v"], [0, TOKENS], [0], case.window, a["sink"],
+                             case.scale, toks, heads, threads=threads)
+            secs += time.perf_counter() - t0
+        return flops, secs
+
+    f, s = run(64)
+    n = int(np.clip(64 * budget_s / max(s, 1e-3), 64, 200000))
+    f, s = run(n)
+    return {"value": f / s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} rows x 2 layers (1 full, 1 window-128) drawn uniformly over the "
+                      f"16k positions and 64 heads, fp64 oracle, {s:.1f} s",
+            "seconds": round(s, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--detail", default=None, help="write per-chunk timings (JSON) here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; a multi-GPU figure is not produced "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gqa_flash_attention_prefill_amd import binding
+    L = binding.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    layers = make_layers(torch, dev)
+    torch.cuda.synchronize()
+
+    # marshal every call's arguments once (pointers + sizes), C ABI calls below
+    calls = []  # (layer, chunk, args)
+    for c in range(N_CHUNKS):
+        for layer, (case, inp, out) in enumerate(layers):
+            q = inp["q"][c * CHUNK:(c + 1) * CHUNK]
+            o = out[c * CHUNK:(c + 1) * CHUNK]
+            cargs = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(inp["k_cache"].data_ptr()),
+                    ctypes.c_void_p(inp["v_cache"].data_ptr()), c * CHUNK, case.window,
+                    ctypes.c_void_p(inp["sink"].data_ptr()), ctypes.c_float(case.scale),
+                    ctypes.c_void_p(o.data_ptr()), CHUNK, H_Q, H_KV, D, TOKENS,
+                    binding.ATTN_F16, binding.ATTN_F16, sptr)
+            calls.append((layer, c, cargs))
+    flops = {(layer, c): useful_flops(c * CHUNK, CHUNK, layer_window(layer))
+             for layer in range(LAYERS) for c in range(N_CHUNKS)}
+    step_flops = sum(flops.values())
+
+    def one_step(events=None):
+        for i, (layer, c, a) in enumerate(calls):
+            if events is not None:
+                events[i][0].record(stream)
+            rc = L.attn_prefill(*a)
+            if rc != 0:
+                raise RuntimeError(f"attn_prefill failed: {binding.attn_last_error()} ({rc})")
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; tuning: {binding.attn_tune_stats()}", file=sys.stderr,
+          flush=True)
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1000.0 * wall / args.steps
+
+    # per-call durations (ms) from events on the launch stream
+    dur = np.zeros((args.steps, len(calls)))
+    for s in range(args.steps):
+        for i in range(len(calls)):
+            dur[s, i] = ev[s][i][0].elapsed_time(ev[s][i][1])
+    mean_call = dur.mean(axis=0)
+    full_idx = [i for i, (layer, c, _) in enumerate(calls) if layer_window(layer) <= 0]
+    win_idx = [i for i, (layer, c, _) in enumerate(calls) if layer_window(layer) > 0]
+    full_flops = sum(flops[(calls[i][0], calls[i][1])] for i in full_idx)
+    win_flops = sum(flops[(calls[i][0], calls[i][1])] for i in win_idx)
+    full_ms = mean_call[full_idx].sum()
+    win_ms = mean_call[win_idx].sum()
+    full_tflops = full_flops / (full_ms * 1e-3) / 1e12
+    win_bytes = sum(algorithmic_bytes(calls[i][1] * CHUNK, CHUNK, WINDOW) for i in win_idx)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_chunk_full = [float(np.mean([mean_call[i] for i in full_idx if calls[i][1] == c])) * 1e3
+                      for c in range(N_CHUNKS)]
+    per_chunk_win = [float(np.mean([mean_call[i] for i in win_idx if calls[i][1] == c])) * 1e3
+                     for c in range(N_CHUNKS)]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu_layers = []
+        for layer in (0, 1):
+            case, inp, _ = layers[layer]
+            cpu_layers.append((case, {k: (v.cpu() if isinstance(v, torch.Tensor) else v)
+                                      for k, v in inp.items()}))
+        cpu = cpu_baseline(torch, cpu_layers)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "16k chunked prefill: 32 chunks of 512 (past_len 0..15872), 24 layers "
+                        "alternating full attention and window 128, H_q=64, H_kv=8, d=64, fp16, "
+                        "per-head sinks",
+            "calls_per_step": len(calls),
+            "full_attn_tflops": round(full_tflops, 2),
+            "full_attn_frac_peak": round(full_tflops / PEAK_TFLOPS_F16, 4),
+            "full_attn_us_per_call": round(1e3 * full_ms / len(full_idx), 2),
+            "full_attn_ms_per_layer": round(full_ms / (len(full_idx) / N_CHUNKS), 3),
+            "window_us_per_call": round(1e3 * win_ms / len(win_idx), 2),
+            "window_hbm_gbs": round(win_bytes / (win_ms * 1e-3) / 1e9, 1),
+            "us_per_layer_call": round(1e3 * (full_ms + win_ms) / len(calls), 2),
+            "attn_ms_per_16k_prefill": round(full_ms + win_ms, 3),
+            "frac_peak_whole_step": round(value / PEAK_TFLOPS_F16, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(full_tflops, 2),
+            "peak": PEAK_TFLOPS_F16,
+            "unit": "TFLOP/s",
+            "frac": round(full_tflops / PEAK_TFLOPS_F16, 4),
+            "traffic": None,
+            "kernel": "full-attention calls (window <= 0)",
+        },
+        "cpu_baseline": cpu,
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"full_us_per_chunk": per_chunk_full, "window_us_per_chunk": per_chunk_win,
+                       "result": result}, f, indent=1)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

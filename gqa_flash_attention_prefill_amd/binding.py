@@ -1,0 +1,187 @@
+"""Python binding of libattn_prefill.so (the C ABI in include/attn_prefill.h).
+
+Argument marshalling only: tensors become device pointers and sizes, the
+current torch stream becomes the hipStream_t, and every step of the
+attention runs in the library's HIP kernels.  There is no fallback: if the
+library is not built, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_prefill.so")
+
+ATTN_OK, ATTN_DECLINED, ATTN_EINVAL, ATTN_EHIP = 0, -1, -2, -3
+ATTN_F16, ATTN_BF16, ATTN_F32 = 1, 2, 3
+ATTN_LOG_FIELDS = 8
+LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last",
+              "n_visited")
+
+_DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
+
+EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_last_error", "attn_tune_stats",
+            "attn_tune_reset", "attn_config_count", "attn_config_name", "attn_force_config")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+class AttnDeclined(AttnError):
+    pass
+
+
+class TileLog(ctypes.Structure):
+    _fields_ = [("records", ctypes.c_void_p), ("capacity", ctypes.c_int64),
+                ("n_records", ctypes.c_int64), ("bkv", ctypes.c_int32),
+                ("q_rows", ctypes.c_int32)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                           "(hipcc for gfx950); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    L.attn_prefill.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, ctypes.c_float, _vp, _i32, _i32,
+                               _i32, _i32, _i32, _i32, _i32, _vp]
+    L.attn_prefill.restype = ctypes.c_int
+    L.attn_prefill_varlen.argtypes = [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp,
+                                      ctypes.c_float, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      ctypes.POINTER(TileLog), _vp]
+    L.attn_prefill_varlen.restype = ctypes.c_int
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_tune_stats.argtypes = [_i64p, _i64p, _i64p]
+    L.attn_tune_stats.restype = ctypes.c_int
+    L.attn_tune_reset.argtypes = []
+    L.attn_tune_reset.restype = None
+    L.attn_config_count.argtypes = []
+    L.attn_config_count.restype = ctypes.c_int32
+    L.attn_config_name.argtypes = [_i32]
+    L.attn_config_name.restype = ctypes.c_char_p
+    L.attn_force_config.argtypes = [_i32]
+    L.attn_force_config.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def _check(code):
+    if code == ATTN_OK:
+        return code
+    msg = attn_last_error()
+    if code == ATTN_DECLINED:
+        raise AttnDeclined(code, msg)
+    raise AttnError(code, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, ndim):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in _DTYPE_CODE:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+
+
+def attn_prefill(q, k_cache, v_cache, past_len, window, head_sink, scale, out, stream=None,
+                 check=True):
+    """One chunk after `past_len` cached keys.  q/out [sq, h_q, d];
+    k_cache/v_cache [1, h_kv, s_cap, d]; head_sink float32 [h_q] or None."""
+    _require(q, "q", 3)
+    _require(out, "out", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    sq, h_q, d = q.shape
+    _, h_kv, s_cap, _ = k_cache.shape
+    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
+        raise ValueError("head_sink must be a contiguous float32 tensor")
+    code = lib().attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(past_len), int(window),
+                              _ptr(head_sink), float(scale), _ptr(out), sq, h_q, h_kv, d, s_cap,
+                              _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream))
+    return _check(code) if check else code
+
+
+def attn_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head_sink, scale,
+                        out, tile_log=None, stream=None, check=True):
+    """Ragged batch.  cu_seqlens_q / past_len are host sequences of ints.
+    tile_log: None, or an int32 device tensor [capacity, 8] that receives the
+    visited-tile records; then the return value is (code, n_records, bkv, q_rows)."""
+    _require(q, "q", 3)
+    _require(out, "out", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    _, h_q, d = q.shape
+    batch, h_kv, s_cap, _ = k_cache.shape
+    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
+    pl = (ctypes.c_int32 * max(1, len(past_len)))(*[int(x) for x in past_len])
+    nseq = len(past_len)
+    if len(cu_seqlens_q) != nseq + 1:
+        raise ValueError("cu_seqlens_q must have len(past_len) + 1 entries")
+    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
+        raise ValueError("head_sink must be a contiguous float32 tensor")
+    log = None
+    if tile_log is not None:
+        if tile_log.dtype != torch.int32 or tile_log.dim() != 2 or tile_log.shape[1] != 8:
+            raise ValueError("tile_log must be an int32 tensor [capacity, 8]")
+        log = TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
+    code = lib().attn_prefill_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
+        float(scale), _ptr(out), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype],
+        ctypes.byref(log) if log is not None else None, _stream(stream))
+    if check:
+        _check(code)
+    if log is not None:
+        return code, log.n_records, log.bkv, log.q_rows
+    return code
+
+
+def attn_tune_stats():
+    s, l, k = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    lib().attn_tune_stats(ctypes.byref(s), ctypes.byref(l), ctypes.byref(k))
+    return {"sweeps": s.value, "tuning_launches": l.value, "cached_keys": k.value}
+
+
+def attn_tune_reset():
+    lib().attn_tune_reset()
+
+
+def attn_config_count():
+    return lib().attn_config_count()
+
+
+def attn_config_name(i):
+    n = lib().attn_config_name(i)
+    return None if n is None else n.decode()
+
+
+def attn_force_config(i):
+    return _check(lib().attn_force_config(i))

@@ -1,0 +1,373 @@
+// C ABI of the gfx950 attention-prefill library: argument checks, declines,
+// the host-side work plan, the tuning cache and the launches.
+//
+// Conventions follow hip-ep pull request 622 ("perf(gqa): support sliding
+// windows in the fused flash prefill kernel"): an unsupported request is
+// declined with -1 before anything is launched, so a caller can fall back
+// instead of getting a wrong result; the tuning cache is keyed on the shape
+// of the call rather than on the growing KV length (commit "tuning key"),
+// with the window in the key (commit "window in v5"), and tuning launches
+// leave the sink out (commit "fold sink into v5 epilogue").
+//
+// Batch metadata (chunk lengths, cached-prefix lengths) stays on the host and
+// travels to the kernel in its arguments: no device allocation, no
+// host-to-device copy and no device-to-host read happen on this path.
+
+#include "attn_prefill.h"
+#include "attn_internal.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <tuple>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  if (getenv("ATTN_PREFILL_DEBUG")) fprintf(stderr, "[attn_prefill] %s (%d)\n", buf, code);
+  return code;
+}
+
+// ---- device check: gfx950 only ---------------------------------------------
+std::mutex g_dev_mu;
+std::map<int, bool> g_dev_ok;
+
+int check_device(int* dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev_ok.find(dev);
+  if (it == g_dev_ok.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(ATTN_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = g_dev_ok.emplace(dev, ok).first;
+  }
+  if (!it->second) return fail(ATTN_DECLINED, "device %d is not gfx950", dev);
+  return ATTN_OK;
+}
+
+// ---- tuning cache --------------------------------------------------------------
+using TuneKey = std::tuple<int, int, int, int64_t, int, int, int, int, int>;
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tune;
+int64_t g_sweeps = 0, g_tune_launches = 0;
+std::atomic<int> g_forced{-1};
+
+int env_forced_config() {
+  const char* s = getenv("ATTN_PREFILL_CONFIG");
+  if (!s || !*s) return -1;
+  for (int i = 0; i < attn::config_count(); ++i)
+    if (strcmp(attn::config(i).name, s) == 0) return i;
+  return -1;
+}
+
+bool tuning_enabled() {
+  const char* s = getenv("ATTN_PREFILL_TUNE");
+  return !(s && strcmp(s, "0") == 0);
+}
+
+// ---- work plan -------------------------------------------------------------
+struct Call {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const float* sink;
+  const int32_t* cu;
+  const int32_t* past;
+  int32_t batch, window, h_q, h_kv, d, s_cap, dtype, out_dtype;
+  float scale;
+  attn_tile_log* log;
+  hipStream_t stream;
+};
+
+int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// Launch every sequence of `c` with configuration `cfg`.  When `log_base` is
+// non-null, records go there (the caller checked the capacity) and the number
+// written is returned in *n_records.
+int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
+               int64_t* n_records) {
+  const attn::KernelConfig& cfg = attn::config(cfg_index);
+  const int group = c.h_q / c.h_kv;
+  const int hpack = gcd_int(group, 32);
+  const int q_rows = cfg.rows / hpack;
+  attn::LaunchFn fn = cfg.fn[c.d == 128][c.dtype == ATTN_BF16][c.out_dtype == ATTN_F32];
+
+  attn::Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = c.q;
+  p.k = c.k;
+  p.v = c.v;
+  p.out = c.out;
+  p.sink = with_sink ? c.sink : nullptr;
+  p.h_q = c.h_q;
+  p.h_kv = c.h_kv;
+  p.group = group;
+  p.hpack = hpack;
+  p.n_hgroups = group / hpack;
+  p.q_rows = q_rows;
+  p.s_cap = c.s_cap;
+  p.window = c.window > 0 ? c.window : 0;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+
+  int64_t written = 0;
+  for (int32_t b0 = 0; b0 < c.batch; b0 += attn::kMaxSeq) {
+    const int32_t nb = std::min<int32_t>(attn::kMaxSeq, c.batch - b0);
+    attn::SeqTable& st = p.seq;
+    st.n_seq = nb;
+    st.cu_tiles[0] = 0;
+    st.cu_q[0] = c.cu[b0];
+    for (int i = 0; i < nb; ++i) {
+      const int32_t sq = c.cu[b0 + i + 1] - c.cu[b0 + i];
+      st.cu_tiles[i + 1] = st.cu_tiles[i] + (sq + q_rows - 1) / q_rows;
+      st.cu_q[i + 1] = c.cu[b0 + i + 1];
+      st.past[i] = c.past[b0 + i];
+      st.slot[i] = b0 + i;
+    }
+    const int64_t n_items = (int64_t)st.cu_tiles[nb] * c.h_kv * p.n_hgroups;
+    if (n_items == 0) continue;
+    if (n_items > 0x7fffffff) return fail(ATTN_EINVAL, "too many work items (%lld)",
+                                          (long long)n_items);
+    p.log = log_base ? log_base + written * ATTN_LOG_FIELDS : nullptr;
+    hipError_t e = fn(p, (int)n_items, c.stream);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    written += n_items;
+  }
+  if (n_records) *n_records = written;
+  return ATTN_OK;
+}
+
+int64_t plan_items(const Call& c, int cfg_index) {
+  const int group = c.h_q / c.h_kv;
+  const int hpack = gcd_int(group, 32);
+  const int q_rows = attn::config(cfg_index).rows / hpack;
+  int64_t tiles = 0;
+  for (int32_t b = 0; b < c.batch; ++b) tiles += (c.cu[b + 1] - c.cu[b] + q_rows - 1) / q_rows;
+  return tiles * c.h_kv * (group / hpack);
+}
+
+// One synchronous sweep: time each configuration on the caller's buffers and
+// stream (the output is overwritten by the real launch that follows).
+int sweep(const Call& c, int* best_out) {
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+    return fail(ATTN_EHIP, "hipEventCreate failed");
+  const int reps = 3;
+  float best_ms = INFINITY;
+  int best = 0;
+  int64_t launches = 0;
+  int rc = ATTN_OK;
+  for (int i = 0; i < attn::config_count() && rc == ATTN_OK; ++i) {
+    rc = run_config(c, i, false, nullptr, nullptr);  // warm-up
+    ++launches;
+    if (rc) break;
+    if (hipEventRecord(e0, c.stream) != hipSuccess) { rc = fail(ATTN_EHIP, "event"); break; }
+    for (int r = 0; r < reps && rc == ATTN_OK; ++r, ++launches)
+      rc = run_config(c, i, false, nullptr, nullptr);
+    if (rc) break;
+    if (hipEventRecord(e1, c.stream) != hipSuccess) { rc = fail(ATTN_EHIP, "event"); break; }
+    if (hipEventSynchronize(e1) != hipSuccess) { rc = fail(ATTN_EHIP, "sweep sync"); break; }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) { rc = fail(ATTN_EHIP, "event"); break; }
+    if (getenv("ATTN_PREFILL_TUNE_DEBUG"))
+      fprintf(stderr, "[attn_prefill tune] %-14s %9.3f us\n", attn::config(i).name,
+              1000.f * ms / reps);
+    if (ms < best_ms) { best_ms = ms; best = i; }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  g_tune_launches += launches;
+  *best_out = best;
+  return rc;
+}
+
+int choose_config(const Call& c, int* cfg) {
+  const int forced = g_forced.load();
+  if (forced >= 0) { *cfg = forced; return ATTN_OK; }
+  const int env = env_forced_config();
+  if (env >= 0) { *cfg = env; return ATTN_OK; }
+  if (!tuning_enabled()) {
+    *cfg = attn::default_config(c.d, c.dtype, c.window);
+    return ATTN_OK;
+  }
+  const int64_t tokens = c.cu[c.batch] - c.cu[0];
+  TuneKey key{c.d, c.dtype, c.out_dtype, tokens, c.h_q, c.h_q / c.h_kv,
+              c.window > 0 ? c.window : 0, c.batch, 0};
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  auto it = g_tune.find(key);
+  if (it != g_tune.end()) { *cfg = it->second; return ATTN_OK; }
+  int best = 0;
+  int rc = sweep(c, &best);
+  if (rc) return rc;
+  ++g_sweeps;
+  g_tune.emplace(key, best);
+  if (getenv("ATTN_PREFILL_TUNE_DEBUG"))
+    fprintf(stderr, "[attn_prefill tune] chose %s\n", attn::config(best).name);
+  *cfg = best;
+  return ATTN_OK;
+}
+
+int validate(const Call& c) {
+  if (c.batch < 0) return fail(ATTN_EINVAL, "batch < 0");
+  if (c.batch > 0 && (!c.cu || !c.past)) return fail(ATTN_EINVAL, "null batch metadata");
+  if (c.h_q <= 0 || c.h_kv <= 0 || c.d <= 0 || c.s_cap < 0)
+    return fail(ATTN_EINVAL, "non-positive size");
+  if (c.h_q % c.h_kv != 0) return fail(ATTN_EINVAL, "h_q %% h_kv != 0");
+  if (c.batch > 0) {
+    if (c.cu[0] != 0) return fail(ATTN_EINVAL, "cu_seqlens_q[0] != 0");
+    for (int32_t b = 0; b < c.batch; ++b) {
+      const int64_t sq = (int64_t)c.cu[b + 1] - c.cu[b];
+      if (sq < 0) return fail(ATTN_EINVAL, "cu_seqlens_q decreases at %d", b);
+      if (c.past[b] < 0) return fail(ATTN_EINVAL, "past_len[%d] < 0", b);
+      if ((int64_t)c.past[b] + sq > c.s_cap)
+        return fail(ATTN_EINVAL, "past_len + sq > s_cap for sequence %d", b);
+    }
+  }
+  const int64_t tokens = c.batch > 0 ? c.cu[c.batch] : 0;
+  if (tokens > 0 && (!c.q || !c.k || !c.v || !c.out))
+    return fail(ATTN_EINVAL, "null tensor pointer");
+  if (c.scale != c.scale || std::isinf(c.scale)) return fail(ATTN_EINVAL, "scale not finite");
+  if (c.log) {
+    if (c.log->capacity < 0 || (c.log->capacity > 0 && !c.log->records))
+      return fail(ATTN_EINVAL, "bad tile log");
+  }
+  // declines: valid requests this library does not implement
+  if (c.d != 64 && c.d != 128) return fail(ATTN_DECLINED, "d=%d not supported (64, 128)", c.d);
+  if (c.dtype != ATTN_F16 && c.dtype != ATTN_BF16)
+    return fail(ATTN_DECLINED, "input dtype %d not supported", c.dtype);
+  if (c.out_dtype != c.dtype && c.out_dtype != ATTN_F32)
+    return fail(ATTN_DECLINED, "out dtype %d not supported for input dtype %d", c.out_dtype,
+                c.dtype);
+  if (tokens > 0) {
+    auto mis = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; };
+    if (mis(c.q) || mis(c.k) || mis(c.v) || mis(c.out))
+      return fail(ATTN_DECLINED, "tensor pointers must be 16-byte aligned");
+  }
+  return ATTN_OK;
+}
+
+int run(const Call& c) {
+  g_last_error.clear();
+  int rc = validate(c);
+  if (rc) return rc;
+  const int64_t tokens = c.batch > 0 ? c.cu[c.batch] : 0;
+  if (tokens == 0) {
+    if (c.log) { c.log->n_records = 0; }
+    return ATTN_OK;
+  }
+  int dev = 0;
+  rc = check_device(&dev);
+  if (rc) return rc;
+  int cfg = 0;
+  rc = choose_config(c, &cfg);
+  if (rc) return rc;
+  int32_t* log_base = nullptr;
+  if (c.log) {
+    const int64_t need = plan_items(c, cfg);
+    if (need > c.log->capacity)
+      return fail(ATTN_EINVAL, "tile log holds %lld records, %lld needed",
+                  (long long)c.log->capacity, (long long)need);
+    log_base = c.log->records;
+    c.log->bkv = attn::config(cfg).bkv;
+    const int hpack = gcd_int(c.h_q / c.h_kv, 32);
+    c.log->q_rows = attn::config(cfg).rows / hpack;
+  }
+  int64_t n = 0;
+  rc = run_config(c, cfg, true, log_base, &n);
+  if (rc) return rc;
+  if (c.log) c.log->n_records = n;
+  if (getenv("ATTN_PREFILL_DEBUG"))
+    fprintf(stderr, "[attn_prefill] config %s, %lld work items\n", attn::config(cfg).name,
+            (long long)plan_items(c, cfg));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void* q, const void* k_cache, const void* v_cache, int32_t past_len,
+                 int32_t window, const float* head_sink, float scale, void* out, int32_t sq,
+                 int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap, int32_t dtype,
+                 int32_t out_dtype, void* stream) {
+  try {
+    if (sq < 0) return fail(ATTN_EINVAL, "sq < 0");
+    const int32_t cu[2] = {0, sq};
+    const int32_t past[1] = {past_len};
+    Call c{q, k_cache, v_cache, out, head_sink, cu, past, 1, window, h_q, h_kv, d, s_cap,
+           dtype, out_dtype, scale, nullptr, reinterpret_cast<hipStream_t>(stream)};
+    return run(c);
+  } catch (...) {
+    return fail(ATTN_EHIP, "internal error");
+  }
+}
+
+int attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
+                        int32_t window, const float* head_sink, float scale, void* out,
+                        int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap, int32_t dtype,
+                        int32_t out_dtype, attn_tile_log* tile_log, void* stream) {
+  try {
+    Call c{q, k_cache, v_cache, out, head_sink, cu_seqlens_q, past_len, batch, window, h_q,
+           h_kv, d, s_cap, dtype, out_dtype, scale, tile_log,
+           reinterpret_cast<hipStream_t>(stream)};
+    return run(c);
+  } catch (...) {
+    return fail(ATTN_EHIP, "internal error");
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  if (sweeps) *sweeps = g_sweeps;
+  if (tuning_launches) *tuning_launches = g_tune_launches;
+  if (cached_keys) *cached_keys = (int64_t)g_tune.size();
+  return ATTN_OK;
+}
+
+void attn_tune_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tune.clear();
+  g_sweeps = 0;
+  g_tune_launches = 0;
+}
+
+int32_t attn_config_count(void) { return attn::config_count(); }
+
+const char* attn_config_name(int32_t i) {
+  if (i < 0 || i >= attn::config_count()) return nullptr;
+  return attn::config(i).name;
+}
+
+int attn_force_config(int32_t i) {
+  if (i < -1 || i >= attn::config_count()) return fail(ATTN_EINVAL, "no configuration %d", i);
+  g_forced.store(i);
+  return ATTN_OK;
+}
+
+}  // extern "C"

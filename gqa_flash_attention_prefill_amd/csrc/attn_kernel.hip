@@ -1,0 +1,491 @@
+// Fused causal grouped-query flash-attention prefill for gfx950 (CDNA 4).
+//
+// What is computed (hip-ep pull request 622, "perf(gqa): support sliding
+// windows in the fused flash prefill kernel"; sgl-project/sglang pull request
+// 34468): for each chunk row at absolute position past + q, softmax over the
+// kept keys k <= past + q and, with a window, k >= past + q - window + 1,
+// with an optional per-head sink logit added to the denominator only.
+//
+// Work decomposition.  One workgroup = one Q tile = NW waves x 32 rows.  The
+// rows of a tile are (chunk position, q head) pairs: `hpack` q heads of one
+// KV group share each position, so one K/V tile staged in LDS serves every
+// head of the group ("no-expand" GQA: KV heads are never replicated).
+//
+// Per KV tile (BKV keys):
+//   * K and V are read from HBM with 16-byte coalesced loads into registers
+//     one stage ahead, then stored to a double-buffered LDS stage (both
+//     row-major, XOR-swizzled in 16-byte chunks); one barrier per stage;
+//   * S^T = K . Q^T on v_mfma_f32_32x32x16_{f16,bf16}: with K as the A operand
+//     and the wave's Q (held in registers for the whole loop) as B, each
+//     lane's accumulator holds ONE query row (lane % 32) and 16 keys, so the
+//     row max is an in-lane reduction plus one exchange with lane ^ 32 and
+//     the rescale of the output accumulator is lane-local;
+//   * mask only on boundary tiles; online softmax in exp2 space (scores are
+//     scaled by scale * log2 e inside the exponent's FMA); the reference max
+//     is raised lazily (only when a row's tile max exceeds it by 2^8), which
+//     skips most accumulator rescales; a row that has seen no key and whose
+//     tile is fully masked keeps m = -inf and is guarded ("window in v5":
+//     exp2(-inf - -inf) would be NaN);
+//   * O^T += V^T . P^T on the same MFMA: P is converted to 16-bit in
+//     registers and used directly as the B operand; V^T comes from the
+//     row-major V tile through the gfx950 transposing LDS read
+//     ds_read_b64_tr_b16.  For bf16 inputs P is split into hi + lo bf16
+//     parts and both are accumulated, since one bf16 rounding of P alone
+//     costs ~1e-3 relative error.
+//   * Two waves per row group (KV splits) take alternate tiles, so each
+//     SIMD holds two independent waves; their partial (m, l, O) are merged
+//     through LDS before the epilogue.
+//
+// KV loop bounds ("window in v5"; sglang 34468 "bound the stage-1 prefix
+// loop"): the loop starts at the tile holding the lowest key the Q tile's
+// FIRST row keeps (lower bounds are non-decreasing within a tile) and ends
+// at the tile holding the LAST row's own key; the per-row mask trims the
+// rest.  Waves skip tiles outside their own rows' range.
+//
+// Epilogue ("fold sink into v5 epilogue"): l += exp2(sink * log2 e - m) when
+// m != -inf; out = acc / max(l, FLT_MIN).
+
+#include "attn_internal.h"
+
+#include <float.h>
+
+namespace attn {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct F16 {
+  static constexpr bool kSplitP = false;
+  __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // round to nearest even (v_cvt_pk_f16_f32)
+  __device__ static uint32_t pack(float x, float y) {
+    f16x2 h = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ static float lo_part(float, uint32_t, int) { return 0.f; }
+  // l + (both fp16 halves of `packed`), accumulated in fp32 (v_dot2c_f32_f16)
+  __device__ static float rowsum(uint32_t packed, float l) {
+    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, l, false);
+  }
+};
+
+struct BF16 {
+  static constexpr bool kSplitP = true;
+  __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // round to nearest even (v_cvt_pk_bf16_f32)
+  __device__ static uint32_t pack(float x, float y) {
+    bf16x2 h = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  // x - (the bf16 value in half `which` of `packed`)
+  __device__ static float lo_part(float x, uint32_t packed, int which) {
+    uint32_t bits = which ? (packed & 0xffff0000u) : (packed << 16);
+    return x - __builtin_bit_cast(float, bits);
+  }
+  __device__ static float rowsum(uint32_t, float l) { return l; }
+};
+
+template <typename TI>
+__device__ inline u32x4 load16(const void* base, int64_t elem_offset) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem_offset);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16-byte-chunk XOR swizzles of the K and V tiles in LDS (both row-major,
+// one key per row).
+//  K: S^T reads 16 bytes per lane with lanes 0..7 on keys 0..7 of one chunk
+//     column -> chunk ^ (key & 7) spreads them over 8 distinct chunks.
+//  V: transposed reads (ds_read_b64_tr_b16) take 4 keys x 32 bytes per 16-lane
+//     group -> pair-of-chunks ^ (key & 3) puts the 4 keys on distinct banks.
+__device__ inline int k_chunk(int key, int c) { return c ^ (key & 7); }
+__device__ inline int v_chunk(int key, int c) { return c ^ ((key & 3) << 1); }
+
+// Lane layout used with v_mfma_f32_32x32x16 (A: 32 rows x 16 k, B: 16 k x 32
+// cols, C: 32 x 32):  A/B lane l holds row/col l % 32 and k = 8 (l / 32) + 0..7;
+// C lane l holds column l % 32 and rows 8 (i / 4) + 4 (l / 32) + (i % 4), i < 16.
+//
+// S^T = K . Q^T puts query (l % 32) in every lane's 16 accumulators, over keys
+// 8 (i / 4) + 4 h + (i % 4) of a 32-key block (h = l / 32).  P = exp2(...) of
+// those 16 values, converted to 16 bits, is directly the B operand (P^T) of
+// two PV steps: step j2 covers keys 16 j2 + {4h .. 4h+3, 8+4h .. 8+4h+3}, in
+// the order of accumulators 8 j2 .. 8 j2 + 7.  The matching A operand (V^T)
+// needs, in lane (d, h), V[key][d] for those 8 keys: two ds_read_b64_tr_b16
+// loads of 4 keys each.  That instruction hands lane i of each 16-lane group
+// element (i % 4) of the 8-byte pieces addressed by lanes 4k + i / 4 (k < 4),
+// so lane j of the group addresses V[key0 + j / 4][d0 + 4 (j % 4) .. + 3] and
+// lane i receives V[key0 + k][d0 + i], k = 0..3.
+template <int D>
+__device__ inline u32x4 v_frag(const u32x4* vt, int g16, int db, int lane) {
+  constexpr int DCH = D / 8;
+  const int j = lane & 15, grp = lane >> 4;
+  const int h = grp >> 1;
+  const int d = db * 32 + (grp & 1) * 16 + 4 * (j & 3);
+  const int key_a = g16 * 16 + 4 * h + (j >> 2);
+  const int key_b = key_a + 8;
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(vt);
+  const uint16_t* pa = base + (key_a * DCH + v_chunk(key_a, d >> 3)) * 8 + (d & 7);
+  const uint16_t* pb = base + (key_b * DCH + v_chunk(key_b, d >> 3)) * 8 + (d & 7);
+  const s16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+  const s16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pb);
+  const u32x2 a2 = __builtin_bit_cast(u32x2, ra), b2 = __builtin_bit_cast(u32x2, rb);
+  return u32x4{a2[0], a2[1], b2[0], b2[1]};
+}
+
+__device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
+
+// Workgroup = R row groups x S KV splits of one wave each.  Row group rg owns
+// 32 Q-tile rows; split sp takes every S-th KV tile of the workgroup's range,
+// so the S waves of a row group (one per SIMD pair slot) work on different
+// tiles at once and are merged through LDS at the end.  K/V for S tiles form
+// one stage; stages are double-buffered in LDS and the next stage's global
+// loads are issued before the current stage's math.
+template <int D, int BKV, int R, int S, bool WIN, typename TI, typename TO>
+__global__ __launch_bounds__(R * S * 64) void attn_fwd_kernel(Params p) {
+  constexpr int NW = R * S;
+  constexpr int NT = NW * 64;
+  constexpr int DCH = D / 8;                // 16-byte chunks per K/V row
+  constexpr int TILE_CH = BKV * DCH;        // chunks of one K (or V) tile
+  constexpr int STAGE_CH = 2 * S * TILE_CH; // K and V of S tiles
+  constexpr int LOADS = STAGE_CH / NT;      // 16-byte loads per thread per stage
+  constexpr int KSTEPS = D / 16;            // MFMA k-steps of Q.K^T
+  constexpr int NB = BKV / 32;              // 32-key blocks per KV tile
+  constexpr int NG = BKV / 16;              // 16-key PV steps per KV tile
+  constexpr int DB = D / 32;                // 32-wide d blocks of the output
+  constexpr float kRescale = 8.f;           // lazy-rescale threshold (log2 units)
+  static_assert(STAGE_CH % NT == 0 && TILE_CH % NT == 0, "loads must tile the stage");
+  static_assert(BKV % 32 == 0 && (D == 64 || D == 128), "tile shape");
+  static_assert(S == 1 || S == 2, "1 or 2 KV splits");
+
+  __shared__ u32x4 lds[2 * STAGE_CH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = wave % R;
+  const int sp = wave / R;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // ---- work item: (KV head, head group, Q tile), heaviest Q tiles first ----
+  const int item = blockIdx.x;
+  const int g = item % p.h_kv;
+  const int r0 = item / p.h_kv;
+  const int hg = r0 % p.n_hgroups;
+  const int tix = p.seq.cu_tiles[p.seq.n_seq] - 1 - r0 / p.n_hgroups;
+  int bi = 0;
+  {
+    int lo = 0, hi = p.seq.n_seq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq.cu_tiles[mid] <= tix) lo = mid; else hi = mid - 1;
+    }
+    bi = lo;
+  }
+  const int sq = p.seq.cu_q[bi + 1] - p.seq.cu_q[bi];
+  const int past = p.seq.past[bi];
+  const int slot = p.seq.slot[bi];
+  const int64_t tok0 = p.seq.cu_q[bi];
+  const int q0 = (tix - p.seq.cu_tiles[bi]) * p.q_rows;
+  const int q_last = min(q0 + p.q_rows, sq) - 1;
+  const int skv = past + sq;
+  const int window = WIN ? p.window : 0;  // compile-time 0 for full attention
+
+  // KV tiles of the whole Q tile: floor from the first row, ceiling from the last
+  const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
+  const int t_lo = lo_key / BKV;
+  const int t_hi = (past + q_last) / BKV;
+  const int n_stages = (t_hi - t_lo + S) / S;
+
+  // ---- this lane's row ----
+  const int row = rg * 32 + col;
+  const int pos = q0 + row / p.hpack;
+  const int head = g * p.group + hg * p.hpack + row % p.hpack;
+  const bool valid = pos < sq;
+  const int row_hi = past + pos;                               // last kept key
+  const int row_lo = window > 0 ? past + pos - window + 1 : 0;  // first kept key
+
+  // ---- this row group's rows: skip tiles none of them keeps ----
+  const int wp0 = q0 + (rg * 32) / p.hpack;
+  const int wp1 = min(q0 + (rg * 32 + 31) / p.hpack, sq - 1);
+  const bool wave_live = wp0 < sq;
+  const int w_lo = window > 0 ? max(0, past + wp0 - window + 1) / BKV : 0;
+  const int w_hi = (past + wp1) / BKV;
+  const int w_full_lo = window > 0 ? past + wp1 - window + 1 : 0;  // max row lower bound
+  const int w_full_hi = past + wp0;                                 // min row upper bound
+
+  // ---- Q^T fragments (B operand), held for the whole KV loop ----
+  u32x4 qf[KSTEPS];
+  {
+    const int64_t qoff = ((tok0 + pos) * p.h_q + head) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk] = valid ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t kv_base = ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
+  const float c = p.scale_log2;
+  const float kNegInf = -__builtin_inff();
+
+  // ---- global -> register -> LDS staging of one stage ----
+  u32x4 pre[LOADS];
+  auto fetch = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = i * NT + tid;
+      const int which = e / TILE_CH;        // (split, tensor)
+      const int within = e % TILE_CH;
+      const int key = within / DCH;
+      const int ch = within % DCH;
+      const int t = t_lo + stage * S + (which >> 1);
+      const int kabs = t * BKV + key;
+      u32x4 val = {0, 0, 0, 0};
+      if (t <= t_hi && kabs < skv)
+        val = load16<TI>((which & 1) ? p.v : p.k, kv_base + (int64_t)kabs * D + ch * 8);
+      pre[i] = val;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = i * NT + tid;
+      const int which = e / TILE_CH;
+      const int within = e % TILE_CH;
+      const int key = within / DCH;
+      const int ch = within % DCH;
+      const int phys = (which & 1) ? v_chunk(key, ch) : k_chunk(key, ch);
+      lds[buf * STAGE_CH + which * TILE_CH + key * DCH + phys] = pre[i];
+    }
+  };
+
+  float m_run = kNegInf;  // reference max of scaled scores (log2 units), lazily raised
+  float l_run = 0.f;      // this lane's partial denominator
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  int n_visited = 0, t_first = -1, t_last = -1;  // what the loop walks (tile log)
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_stages; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_stages) fetch(j + 1);
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int ts = t_lo + j * S + s2;
+      if (ts <= t_hi) {
+        if (t_first < 0) t_first = ts;
+        t_last = ts;
+        ++n_visited;
+      }
+    }
+
+    const int t = t_lo + j * S + sp;
+    if (wave_live && t <= t_hi && t >= w_lo && t <= w_hi) {
+      const u32x4* kt = lds + buf * STAGE_CH + (2 * sp) * TILE_CH;
+      const u32x4* vt = kt + TILE_CH;
+      const int kbase = t * BKV;
+
+      // ---- S^T = K . Q^T ----
+      f32x16 s[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        s[nb] = f32x16{};
+        const int kr = nb * 32 + col;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+          s[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, 2 * kk + half)], qf[kk], s[nb]);
+      }
+
+      // ---- mask (boundary tiles only) ----
+      const bool interior = (kbase + BKV - 1 <= w_full_hi) && (kbase >= w_full_lo);
+      if (!interior) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + nb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            if (key > row_hi || key < row_lo) s[nb][i] = kNegInf;
+          }
+      }
+
+      // ---- online softmax in exp2 space, lazily rescaled ----
+      float mx = kNegInf;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[nb][i], s[nb][i + 1]));
+      mx = fmaxf(mx, other_half(mx)) * c;
+      // Raise the reference max only when some row's tile max exceeds it by
+      // more than 2^kRescale (then P <= 2^kRescale stays well inside fp16).
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      // all-masked guard: a row that has seen no key keeps m = -inf; its
+      // scores in this tile are all -inf, so subtracting 0 yields p = 0
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+
+      u32x4 pb[NG];
+      u32x4 pl[NG];
+#pragma unroll
+      for (int g16 = 0; g16 < NG; ++g16)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int i = (g16 & 1) * 8 + w * 2;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g16 >> 1][i], c, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g16 >> 1][i + 1], c, -m_use));
+          const uint32_t hi = TI::pack(p0, p1);
+          pb[g16][w] = hi;
+          if constexpr (TI::kSplitP) {
+            pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
+            l_run += p0 + p1;
+          } else {
+            l_run = TI::rowsum(hi, l_run);
+          }
+        }
+
+      // ---- O^T += V^T . P^T ----
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g16 = 0; g16 < NG; ++g16) {
+          const u32x4 a = v_frag<D>(vt, g16, db, lane);
+          acc[db] = TI::mma(a, pb[g16], acc[db]);
+          if constexpr (TI::kSplitP) acc[db] = TI::mma(a, pl[g16], acc[db]);
+        }
+    }
+
+    if (j + 1 < n_stages) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- merge the KV splits of each row group through LDS ----
+  if constexpr (S > 1) {
+    constexpr int NV = 2 + 16 * DB;
+    float* mb = reinterpret_cast<float*>(lds);
+    if (sp == 1) {
+      float* dst = mb + rg * NV * 64 + lane;
+      dst[0] = m_run;
+      dst[64] = l_run;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(2 + db * 16 + i) * 64] = acc[db][i];
+    }
+    __syncthreads();
+    if (sp == 0) {
+      const float* src = mb + rg * NV * 64 + lane;
+      const float m1 = src[0], l1 = src[64];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[db][i] = a0 * acc[db][i] + a1 * src[(2 + db * 16 + i) * 64];
+      m_run = m;
+    }
+  }
+
+  // ---- epilogue: combine lane halves, fold the sink, normalise, store ----
+  if (sp == 0) {
+    float l_tot = l_run + other_half(l_run);
+    if (p.sink != nullptr && m_run != kNegInf) {
+      const float sk = p.sink[head];
+      l_tot += __builtin_amdgcn_exp2f(sk * kLog2e - m_run);
+    }
+    const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
+
+    if (valid) {
+      const int64_t ooff = ((tok0 + pos) * p.h_q + head) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = db * 32 + i4 * 8 + half * 4;
+          const float o0 = acc[db][i4 * 4 + 0] * inv, o1 = acc[db][i4 * 4 + 1] * inv;
+          const float o2 = acc[db][i4 * 4 + 2] * inv, o3 = acc[db][i4 * 4 + 3] * inv;
+          if constexpr (sizeof(TO) == 4) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
+                f32x4{o0, o1, o2, o3};
+          } else {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
+                u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
+          }
+        }
+    }
+  }
+
+  if (p.log != nullptr && tid == 0) {
+    int32_t* rec = p.log + (int64_t)blockIdx.x * 8;
+    rec[0] = slot;
+    rec[1] = g * p.group + hg * p.hpack;
+    rec[2] = p.hpack;
+    rec[3] = q0;
+    rec[4] = q_last;
+    rec[5] = t_first;
+    rec[6] = t_last;
+    rec[7] = n_visited;
+  }
+}
+
+template <int D, int BKV, int R, int S, typename TI, typename TO>
+hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
+  if (p.window > 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, true, TI, TO>), dim3(n_items),
+                       dim3(R * S * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, false, TI, TO>), dim3(n_items),
+                       dim3(R * S * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int BKV, int R, int S>
+constexpr KernelConfig make_config(const char* name) {
+  return KernelConfig{
+      name, BKV, R * 32,
+      {{{launch<64, BKV, R, S, F16, uint16_t>, launch<64, BKV, R, S, F16, float>},
+        {launch<64, BKV, R, S, BF16, uint16_t>, launch<64, BKV, R, S, BF16, float>}},
+       {{launch<128, BKV, R, S, F16, uint16_t>, launch<128, BKV, R, S, F16, float>},
+        {launch<128, BKV, R, S, BF16, uint16_t>, launch<128, BKV, R, S, BF16, float>}}}};
+}
+
+const KernelConfig kConfigs[] = {
+    make_config<64, 4, 2>("r128_kv64_s2"),
+    make_config<64, 4, 1>("r128_kv64_s1"),
+};
+
+}  // namespace
+
+int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
+const KernelConfig& config(int i) { return kConfigs[i]; }
+int default_config(int /*d*/, int /*dtype*/, int /*window*/) { return 0; }
+
+}  // namespace attn

@@ -1,0 +1,158 @@
+/*
+ * attn_prefill.h -- C ABI of the MI355X (gfx950) fused causal grouped-query
+ * flash-attention prefill library (libattn_prefill.so).
+ *
+ * The operation.  For each sequence b, q head h (reading KV head
+ * h / (h_q / h_kv)), and chunk row q in [0, sq_b) at absolute position
+ * past_len[b] + q:
+ *
+ *   keep key k  iff  k <= past_len + q  and  (window <= 0 or
+ *                                             k >= past_len + q - window + 1)
+ *   s_k   = scale * <q_row, k_k>                      (kept keys only)
+ *   out   = sum_k exp(s_k - m) v_k / ( sum_k exp(s_k - m) + exp(sink_h - m) )
+ *
+ * with m the row maximum; a row without sink drops the exp(sink_h - m) term.
+ * Sources: "perf(gqa): support sliding windows in the fused flash prefill
+ * kernel" (ROCm/hip-ep pull request 622), commit "window in v5" for the
+ * per-row window lower bound and the KV-loop start tile, commit "fold sink
+ * into v5 epilogue" for the sink in the softmax denominator and the clamped
+ * denominator of fully masked rows, and the "Why" section of its body for
+ * chunked prefill over a cached prefix; sgl-project/sglang pull request
+ * 34468, commit "bound the stage-1 prefix loop", for the tile floor over a
+ * full (unbounded) cached prefix.
+ *
+ * Common conventions for every entry point:
+ *  - Device pointers are caller-owned HIP device allocations on the current
+ *    device; the library never allocates, frees or copies device memory on
+ *    this path and never copies device-to-host.
+ *  - All tensors are dense row-major with the innermost dimension contiguous,
+ *    and every tensor base pointer must be 16-byte aligned:
+ *      q, out            [tokens, h_q, d]        tokens = sum of chunk lengths
+ *      k_cache, v_cache  [batch, h_kv, s_cap, d]
+ *    The caller has already written the chunk's own keys/values at cache
+ *    positions [past_len[b], past_len[b] + sq_b); the library only reads the
+ *    cache positions [0, past_len[b] + sq_b) of sequence b and never reads a
+ *    position at or beyond that (positions up to s_cap may hold anything).
+ *  - head_sink: device float32 [h_q] sink logits in the units of the scaled
+ *    scores, or NULL for no sink.  An entry of -INFINITY disables the sink
+ *    for that head.
+ *  - scale multiplies q.k (typically 1/sqrt(d)).
+ *  - window <= 0 means no window; window = 1 keeps only the diagonal key.
+ *  - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns without synchronising, except the first call
+ *    for a new tuning key, which runs a synchronous tuning sweep on that
+ *    stream (see attn_tune_stats).
+ *  - Return codes: ATTN_OK; ATTN_DECLINED (-1): the request is valid but not
+ *    supported (d not 64/128, dtype not f16/bf16, out dtype neither the input
+ *    dtype nor f32, misaligned pointers, device not gfx950) -- nothing is
+ *    launched and out is untouched, so the caller can fall back; ATTN_EINVAL
+ *    (-2): invalid arguments (null pointers, non-positive sizes, h_q not a
+ *    multiple of h_kv, past_len < 0, past_len + sq > s_cap, cu_seqlens not
+ *    starting at 0 or decreasing, tile log too small); ATTN_EHIP (-3): a HIP
+ *    runtime error.  attn_last_error() describes the last non-zero return of
+ *    the calling thread.  No C++ exception crosses this interface.
+ *  - Thread safety: calls may come from several threads; the tuning cache is
+ *    guarded by a mutex.
+ */
+#ifndef ATTN_PREFILL_H
+#define ATTN_PREFILL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ATTN_OK = 0, ATTN_DECLINED = -1, ATTN_EINVAL = -2, ATTN_EHIP = -3 };
+enum { ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_F32 = 3 };
+
+/* Fields of one visited-tile record (int32 each). */
+enum {
+  ATTN_LOG_B = 0,        /* sequence index                                   */
+  ATTN_LOG_H_FIRST = 1,  /* first q head of the work item                    */
+  ATTN_LOG_N_HEADS = 2,  /* q heads the work item covers (h_first ...)       */
+  ATTN_LOG_Q_FIRST = 3,  /* first chunk row of the Q tile                    */
+  ATTN_LOG_Q_LAST = 4,   /* last chunk row of the Q tile (inclusive)         */
+  ATTN_LOG_T_FIRST = 5,  /* first KV tile the loop visited                   */
+  ATTN_LOG_T_LAST = 6,   /* last KV tile the loop visited                    */
+  ATTN_LOG_N_VISITED = 7,/* KV tiles the loop visited                        */
+  ATTN_LOG_FIELDS = 8
+};
+
+/*
+ * Optional record of the KV tiles each work item's loop visited, for
+ * checking the tile floor ("window in v5": the loop starts at the first tile
+ * the Q tile's first row can reach; the causal ceiling is the tile holding
+ * the last row's own key).  KV tile t holds keys [t * bkv, (t + 1) * bkv) of
+ * its sequence.
+ *   records   device int32 [capacity * ATTN_LOG_FIELDS], caller-owned
+ *   capacity  records available; tokens * h_q always suffices
+ *   n_records out: records written (one per work item, in no set order)
+ *   bkv       out: keys per KV tile
+ *   q_rows    out: chunk rows per Q tile
+ */
+typedef struct attn_tile_log {
+  int32_t* records;
+  int64_t capacity;
+  int64_t n_records;
+  int32_t bkv;
+  int32_t q_rows;
+} attn_tile_log;
+
+/*
+ * One sequence: a chunk of sq query rows after past_len cached keys.
+ *   q        [sq, h_q, d]            dtype
+ *   k_cache  [1, h_kv, s_cap, d]     dtype   (keys [0, past_len + sq) valid)
+ *   v_cache  [1, h_kv, s_cap, d]     dtype
+ *   out      [sq, h_q, d]            out_dtype (dtype or ATTN_F32)
+ * sq = 0 is a valid no-op.
+ */
+int attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                 int32_t past_len, int32_t window, const float* head_sink, float scale,
+                 void* out,
+                 int32_t sq, int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                 int32_t dtype, int32_t out_dtype, void* stream);
+
+/*
+ * Ragged batch: sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * of q/out and cache slot b, with past_len[b] cached keys before its chunk.
+ *   cu_seqlens_q  HOST int32 [batch + 1], cu_seqlens_q[0] = 0, non-decreasing
+ *   past_len      HOST int32 [batch]
+ *   tile_log      NULL, or a record to fill (see attn_tile_log)
+ * Chunks of length 0 are allowed; batch = 0 is a no-op.  The metadata stays
+ * on the host: nothing is copied to or from the device for it.
+ */
+int attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
+                        int32_t window, const float* head_sink, float scale, void* out,
+                        int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                        int32_t dtype, int32_t out_dtype,
+                        attn_tile_log* tile_log, void* stream);
+
+/* Text describing the last non-zero return on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Tuning cache ("tuning key" commit of hip-ep pull request 622: keyed on
+ * (d, sq, H_q, G) rather than the growing KV length, plus the window, which
+ * caps the tiles a block walks).  Here the key is (d, dtype, out dtype, q
+ * tokens of the call, h_q, group size, window, batch).  The first call for a
+ * key times every kernel configuration once (a synchronous sweep on the
+ * caller's stream, without the sink) and keeps the fastest; later calls with
+ * the same key reuse it.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and
+ * uses the default configuration; ATTN_PREFILL_CONFIG=<name> forces one.
+ */
+int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys);
+void attn_tune_reset(void);
+
+/* Kernel configurations: count, name of index i (NULL if out of range), and
+ * forcing one for all later calls of this process (index -1 clears). */
+int32_t attn_config_count(void);
+const char* attn_config_name(int32_t i);
+int attn_force_config(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFILL_H */

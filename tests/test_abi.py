@@ -1,0 +1,117 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/attn_prefill.h declares, and turns invalid or unsupported requests
+into EINVAL (-2) / DECLINED (-1) before any HIP call (so no device is
+needed to see them)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_flash_attention_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_prefill.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_exports_every_declared_function(L):
+    declared = _declared_functions()
+    assert "attn_prefill" in declared and "attn_prefill_varlen" in declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(binding.EXPORTED) == declared
+
+
+def _call(L, *, q=FAKE, k=FAKE, v=FAKE, out=FAKE, past=0, window=-1, sink=None, scale=0.125,
+          sq=16, h_q=8, h_kv=2, d=64, s_cap=64, dtype=1, out_dtype=1):
+    return L.attn_prefill(q, k, v, past, window, sink, scale, out, sq, h_q, h_kv, d, s_cap,
+                          dtype, out_dtype, None)
+
+
+def _varlen(L, cu, past, *, window=-1, h_q=8, h_kv=2, d=64, s_cap=64, log=None, ptr=FAKE):
+    cu_a = (ctypes.c_int32 * len(cu))(*cu)
+    pl_a = (ctypes.c_int32 * max(1, len(past)))(*past)
+    return L.attn_prefill_varlen(ptr, ptr, ptr, cu_a, pl_a, len(past), window, None, 0.125, ptr,
+                                 h_q, h_kv, d, s_cap, 1, 1, log, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h_q=6, h_kv=4), binding.ATTN_EINVAL),          # h_q not a multiple of h_kv
+    (dict(past=-1), binding.ATTN_EINVAL),
+    (dict(past=60, sq=16, s_cap=64), binding.ATTN_EINVAL),  # past + sq > s_cap
+    (dict(q=None), binding.ATTN_EINVAL),
+    (dict(out=None), binding.ATTN_EINVAL),
+    (dict(sq=-3), binding.ATTN_EINVAL),
+    (dict(h_q=0), binding.ATTN_EINVAL),
+    (dict(scale=float("nan")), binding.ATTN_EINVAL),
+    (dict(d=96), binding.ATTN_DECLINED),                  # head dim not implemented
+    (dict(d=256), binding.ATTN_DECLINED),
+    (dict(dtype=3, out_dtype=3), binding.ATTN_DECLINED),  # f32 inputs
+    (dict(dtype=1, out_dtype=2), binding.ATTN_DECLINED),  # f16 in, bf16 out
+    (dict(q=MISALIGNED), binding.ATTN_DECLINED),
+])
+def test_rejects_before_touching_a_device(L, kw, code):
+    assert _call(L, **kw) == code
+    assert binding.attn_last_error() != ""
+
+
+def test_empty_chunk_is_a_noop(L):
+    assert _call(L, sq=0, q=None, k=None, v=None, out=None) == binding.ATTN_OK
+    assert _varlen(L, [0], []) == binding.ATTN_OK
+    assert _varlen(L, [0, 0, 0], [3, 5], ptr=None) == binding.ATTN_OK
+
+
+@pytest.mark.parametrize("cu,past,s_cap", [
+    ([1, 5], [0], 64),          # cu_seqlens must start at 0
+    ([0, 8, 4], [0, 0], 64),    # decreasing
+    ([0, 8, 20], [0, 50], 61),  # second sequence: 50 + 12 keys > capacity 61
+    ([0, 8], [-2], 64),         # negative cached prefix
+])
+def test_varlen_metadata_checks(L, cu, past, s_cap):
+    assert _varlen(L, cu, past, s_cap=s_cap) == binding.ATTN_EINVAL
+
+
+def test_tile_log_must_be_usable(L):
+    log = binding.TileLog(None, 4, 0, 0, 0)   # capacity without storage
+    assert _varlen(L, [0, 8], [0], log=ctypes.byref(log)) == binding.ATTN_EINVAL
+
+
+def test_configs_are_named(L):
+    n = binding.attn_config_count()
+    assert n >= 1
+    names = [binding.attn_config_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert binding.attn_config_name(n) is None
+    with pytest.raises(binding.AttnError):
+        binding.attn_force_config(n)
+    binding.attn_force_config(-1)
+
+
+def test_tuning_stats_start_empty(L):
+    binding.attn_tune_reset()
+    st = binding.attn_tune_stats()
+    assert st == {"sweeps": 0, "tuning_launches": 0, "cached_keys": 0}
+
+
+def test_binding_refuses_bad_tensors():
+    import torch
+    q = torch.zeros(4, 2, 64, dtype=torch.float16)
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        binding.attn_prefill(q.transpose(0, 1), k, k, 0, -1, None, 0.1, q)
+    with pytest.raises(ValueError):
+        binding.attn_prefill(q[0], k, k, 0, -1, None, 0.1, q)

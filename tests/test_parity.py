@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Bar: relL2 <= 1e-3 for the fp32 output and for the
+fp16/bf16 output against the oracle rounded to that dtype; the visited-tile
+records equal the tile-floor formula exactly; no NaN anywhere (cache
+positions past each sequence's keys hold NaN, so a stray read shows)."""
+import numpy as np
+import pytest
+import torch
+
+from parity_helpers import (TOL, binding, check_tile_log, f64, oracle_full, oracle_rows, rel_l2,
+                            rne, run_gpu, sample_rows, synth, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    binding.lib()
+    yield
+
+
+def _full_check(case, out_dtypes=("same", "f32"), log=True):
+    inp = synth.make(case)
+    dev = to_device(inp)
+    ref = oracle_full(inp)
+    for od in out_dtypes:
+        tdt = case.torch_dtype if od == "same" else torch.float32
+        cap = case.tokens * case.h_q if log else 0
+        out, recs, bkv, q_rows = run_gpu(dev, out_dtype=tdt, log_capacity=cap)
+        got = f64(out)
+        assert np.all(np.isfinite(got)), f"{case.name}: non-finite output"
+        expect = ref if tdt == torch.float32 else rne(ref, tdt)
+        err = rel_l2(got, expect)
+        print(f"{case.name} out={od}: relL2 {err:.3e}")
+        assert err <= TOL, (case.name, od, err)
+        if log:
+            check_tile_log(recs, bkv, q_rows, case.cu_seqlens, case.past, case.window, case.h_q)
+    return ref
+
+
+def test_tiny_config():
+    _full_check(synth.tiny())
+
+
+MID = [
+    # (name, h_q, h_kv, d, sq, past, window, dtype, sink)
+    ("g4_w100_past700", 8, 2, 64, [333], [700], 100, "f16", True),
+    ("g4_nowin_past700", 8, 2, 64, [333], [700], -1, "f16", True),
+    ("g4_w128_past0", 8, 2, 64, [333], [0], 128, "f16", True),
+    ("g4_w129", 8, 2, 64, [257], [129], 129, "f16", False),
+    ("g4_w1", 8, 2, 64, [100], [37], 1, "f16", True),
+    ("g4_wide", 8, 2, 64, [100], [37], 5000, "f16", True),
+    ("g8_w128_past8192", 16, 2, 64, [130], [8192], 128, "f16", True),
+    ("g8_d128_bf16", 16, 2, 128, [300], [450], 128, "bf16", True),
+    ("g8_d128_bf16_nowin", 16, 2, 128, [300], [450], -1, "bf16", True),
+    ("g8_d128_f16", 16, 2, 128, [190], [65], 100, "f16", True),
+    ("g8_d64_bf16", 16, 2, 64, [190], [65], 63, "bf16", True),
+    ("g1_mha", 4, 4, 64, [150], [90], 65, "f16", True),
+    ("g3_odd_group", 6, 2, 64, [150], [90], 100, "f16", True),
+    ("g16", 16, 1, 64, [77], [200], 33, "f16", True),
+    ("g64_mqa", 64, 1, 64, [40], [100], -1, "f16", True),
+    ("ragged_f16", 8, 2, 64, [1, 0, 77, 200, 5], [0, 5, 300, 64, 1000], 100, "f16", True),
+    ("ragged_bf16_d128", 8, 1, 128, [129, 3, 64], [0, 700, 1], -1, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("spec", MID, ids=[m[0] for m in MID])
+def test_mid_cases(spec):
+    name, h_q, h_kv, d, sq, past, window, dtype, sink = spec
+    case = synth.Case(name, h_q=h_q, h_kv=h_kv, d=d, sq=sq, past=past, window=window,
+                      dtype=dtype, sink=sink, seed=77 + sum(sq) + sum(past),
+                      s_cap=max(p + s for p, s in zip(past, sq)) + 23)
+    _full_check(case)
+
+
+def _each_config():
+    """Yield every kernel configuration, forced for the calls made meanwhile
+    (bitwise properties hold within one configuration; the tuner may pick
+    different ones for different call shapes)."""
+    try:
+        for cfg in range(binding.attn_config_count()):
+            binding.attn_force_config(cfg)
+            yield cfg
+    finally:
+        binding.attn_force_config(-1)
+
+
+def test_wide_window_equals_causal_bitwise():
+    # hip-ep #622 "harness: window cases": a window wider than the sequence
+    # must reproduce full attention exactly
+    case = synth.Case("wide", h_q=8, h_kv=2, d=64, sq=[300], past=[200], window=-1, seed=5)
+    dev = to_device(synth.make(case))
+    for cfg in _each_config():
+        dev["window"] = -1
+        a, _, _, _ = run_gpu(dev)
+        dev["window"] = 500
+        b, _, _, _ = run_gpu(dev)
+        dev["window"] = 10 ** 6
+        c, _, _, _ = run_gpu(dev)
+        assert torch.equal(a, b) and torch.equal(a, c), cfg
+
+
+def test_sink_minus_inf_equals_no_sink_bitwise():
+    case = synth.Case("sinkinf", h_q=8, h_kv=2, d=64, sq=[200], past=[100], window=64, seed=6)
+    dev = to_device(synth.make(case))
+    for cfg in _each_config():
+        dev["sink"] = None
+        a, _, _, _ = run_gpu(dev)
+        dev["sink"] = torch.full((8,), float("-inf"), dtype=torch.float32, device="cuda")
+        b, _, _, _ = run_gpu(dev)
+        assert torch.equal(a, b), cfg
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_window_one_returns_own_value_row(dtype):
+    # hip-ep #622 "harness: window cases": window 1 -> each query sees only itself
+    case = synth.Case("w1", h_q=8, h_kv=2, d=64, sq=[150], past=[40], window=1, sink=False,
+                      dtype=dtype, seed=8)
+    inp = synth.make(case)
+    out, _, _, _ = run_gpu(to_device(inp))
+    v = inp["v_cache"][0]                    # [h_kv, cap, d]
+    expect = v[:, 40:190].permute(1, 0, 2).repeat_interleave(4, dim=1)
+    assert torch.equal(out.cpu(), expect)
+
+
+def test_chunk_rows_match_whole_prefill_rows_bitwise():
+    # chunk rows at past c0 equal rows [c0, c0 + sq) of one prefill over the
+    # whole sequence; bitwise under one kernel configuration (KV tiles are
+    # aligned to key 0 of the sequence and Q tiles to multiples of their rows)
+    case = synth.Case("chunks", h_q=8, h_kv=2, d=64, sq=[640], past=[0], window=100, seed=9,
+                      poison_tail=False)
+    inp = synth.make(case)
+    dev = to_device(inp)
+    for cfg in _each_config():
+        whole, _, _, _ = run_gpu(dev, out_dtype=torch.float32)
+        for c0 in (0, 128, 384):
+            part, _, _, _ = run_gpu(dev, out_dtype=torch.float32,
+                                    q=dev["q"][c0:c0 + 128].contiguous(), cu=[0, 128], past=[c0])
+            assert torch.equal(part, whole[c0:c0 + 128]), (cfg, c0)
+
+
+def test_declined_request_leaves_output_untouched():
+    q = torch.randn(16, 4, 96, device="cuda", dtype=torch.float16)
+    k = torch.randn(1, 2, 16, 96, device="cuda", dtype=torch.float16)
+    out = torch.full_like(q, 3.0)
+    code = binding.attn_prefill(q, k, k, 0, -1, None, 0.1, out, check=False)
+    torch.cuda.synchronize()
+    assert code == binding.ATTN_DECLINED
+    assert torch.all(out == 3.0)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: the whole call runs on the GPU, sampled rows are
+# checked against the oracle one by one.
+# ---------------------------------------------------------------------------
+def _sampled_check(case, n_rows=160, seed=0, q=None, cu=None, past=None, inp=None):
+    inp = inp or synth.make(case)
+    dev = to_device(inp)
+    qd = None if q is None else q.cuda()
+    out, recs, bkv, q_rows = run_gpu(dev, out_dtype=torch.float32, q=qd, cu=cu, past=past,
+                                     log_capacity=(q if q is not None else inp["q"]).shape[0]
+                                     * case.h_q)
+    cu = inp["cu_seqlens"] if cu is None else cu
+    past = inp["past_len"] if past is None else past
+    tokens = cu[-1]
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(seed)
+    must = [0, tokens - 1] + [c for c in cu[1:-1]]
+    toks, heads = sample_rows(rng, tokens, case.h_q, n_rows, must=must)
+    ref = oracle_rows(inp, toks, heads, q=q, cu=cu, past=past)
+    got = f64(out)[toks, heads]
+    err = rel_l2(got, ref)
+    print(f"{case.name}: sampled relL2 {err:.3e} over {len(toks)} rows")
+    assert err <= TOL
+    check_tile_log(recs, bkv, q_rows, cu, past, case.window, case.h_q)
+
+
+def test_full_attention_sq4096():
+    _sampled_check(synth.full_sq4096())
+
+
+@pytest.mark.parametrize("past", [0, 512, 8192])
+def test_sliding_window_chunk512(past):
+    _sampled_check(synth.swa_chunk(past))
+
+
+def test_ragged_batch_bf16_d128():
+    _sampled_check(synth.ragged_bf16(), n_rows=240)
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_chunked_16k_layer(layer):
+    case = synth.chunked16k_layer(layer)
+    inp = synth.make(case)
+    C = synth.CHUNKED16K_CHUNK
+    for c in (0, 1, 15, 31):
+        q = inp["q"][c * C:(c + 1) * C].contiguous()
+        _sampled_check(case, n_rows=64, seed=c, q=q, cu=[0, C], past=[c * C], inp=inp)
