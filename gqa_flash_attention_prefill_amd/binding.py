@@ -11,7 +11,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libattn_prefill.so")
+# ATTN_PREFILL_LIB may name another build of the same library (A/B timing).
+LIB_PATH = os.environ.get("ATTN_PREFILL_LIB") or os.path.join(_HERE, "libattn_prefill.so")
 
 ATTN_OK, ATTN_DECLINED, ATTN_EINVAL, ATTN_EHIP = 0, -1, -2, -3
 ATTN_F16, ATTN_BF16, ATTN_F32 = 1, 2, 3

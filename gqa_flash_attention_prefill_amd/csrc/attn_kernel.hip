@@ -49,6 +49,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
@@ -65,6 +67,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct F16 {
   static constexpr bool kSplitP = false;
+  // Q is pre-scaled by scale * log2(e) (one extra fp16 rounding of q, ~1e-4
+  // relative in p, the size of P's own rounding) so that S^T arrives in exp2
+  // units and the running max can enter through the MFMA accumulator input.
+  static constexpr bool kPrescaleQ = true;
   __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -84,6 +90,7 @@ struct F16 {
 
 struct BF16 {
   static constexpr bool kSplitP = true;
+  static constexpr bool kPrescaleQ = false;  // a bf16 rounding of q*c would cost ~1e-3
   __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -231,60 +238,91 @@ __global__ __launch_bounds__(R * S * 64) void attn_fwd_kernel(Params p) {
   const int w_full_lo = window > 0 ? past + wp1 - window + 1 : 0;  // max row lower bound
   const int w_full_hi = past + wp0;                                 // min row upper bound
 
+  const float c = p.scale_log2;
+  const float kNegInf = -__builtin_inff();
+
   // ---- Q^T fragments (B operand), held for the whole KV loop ----
   u32x4 qf[KSTEPS];
   {
     const int64_t qoff = ((tok0 + pos) * p.h_q + head) * D + half * 8;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      qf[kk] = valid ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const u32x4 v = valid ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
+      if constexpr (TI::kPrescaleQ) {
+        const f16x8 h8 = __builtin_bit_cast(f16x8, v);
+        f16x8 o8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = (_Float16)((float)h8[e] * c);
+        qf[kk] = __builtin_bit_cast(u32x4, o8);
+      } else {
+        qf[kk] = v;
+      }
+    }
   }
 
   const int64_t kv_base = ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
-  const float c = p.scale_log2;
-  const float kNegInf = -__builtin_inff();
+  const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
+  const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
 
   // ---- global -> register -> LDS staging of one stage ----
+  // Thread tid moves chunks tid, tid + NT, ... of every (split, tensor) tile.
+  // Keys at or past skv are loaded from a clamped (valid) address and zeroed
+  // when stored to LDS (not at load time, so the loads stay in flight across
+  // the current stage's math).
+  constexpr int PASSES = TILE_CH / NT;
   u32x4 pre[LOADS];
   auto fetch = [&](int stage) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int e = i * NT + tid;
-      const int which = e / TILE_CH;        // (split, tensor)
-      const int within = e % TILE_CH;
-      const int key = within / DCH;
-      const int ch = within % DCH;
-      const int t = t_lo + stage * S + (which >> 1);
-      const int kabs = t * BKV + key;
-      u32x4 val = {0, 0, 0, 0};
-      if (t <= t_hi && kabs < skv)
-        val = load16<TI>((which & 1) ? p.v : p.k, kv_base + (int64_t)kabs * D + ch * 8);
-      pre[i] = val;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int t = t_lo + stage * S + s2;
+      if (t > t_hi) continue;  // workgroup-uniform
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int within = ps * NT + tid;
+        const int key = within / DCH;
+        const int ch = within % DCH;
+        const int kabs = min(t * BKV + key, skv - 1);
+        const int64_t off = (int64_t)kabs * D + ch * 8;
+        pre[(s2 * 2 + 0) * PASSES + ps] = *reinterpret_cast<const u32x4*>(kptr + off);
+        pre[(s2 * 2 + 1) * PASSES + ps] = *reinterpret_cast<const u32x4*>(vptr + off);
+      }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, int stage) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int e = i * NT + tid;
-      const int which = e / TILE_CH;
-      const int within = e % TILE_CH;
-      const int key = within / DCH;
-      const int ch = within % DCH;
-      const int phys = (which & 1) ? v_chunk(key, ch) : k_chunk(key, ch);
-      lds[buf * STAGE_CH + which * TILE_CH + key * DCH + phys] = pre[i];
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int t = t_lo + stage * S + s2;
+      if (t > t_hi) continue;
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int within = ps * NT + tid;
+        const int key = within / DCH;
+        const int ch = within % DCH;
+        const bool ok = t * BKV + key < skv;
+        u32x4* base = lds + buf * STAGE_CH + (s2 * 2) * TILE_CH + key * DCH;
+        base[k_chunk(key, ch)] = ok ? pre[(s2 * 2 + 0) * PASSES + ps] : u32x4{0, 0, 0, 0};
+        base[TILE_CH + v_chunk(key, ch)] =
+            ok ? pre[(s2 * 2 + 1) * PASSES + ps] : u32x4{0, 0, 0, 0};
+      }
     }
   };
 
-  float m_run = kNegInf;  // reference max of scaled scores (log2 units), lazily raised
-  float l_run = 0.f;      // this lane's partial denominator
+  // Running state per row (this lane's query): m_run is the reference max of
+  // the scaled scores in log2 units.  It is exact after a row's first kept
+  // tile and afterwards raised only when a tile would push p = exp2(s - m_run)
+  // past the fp16 range (the tile is then redone against the new max).
+  float m_run = kNegInf;
+  float l_run = 0.f;      // this lane's partial denominator (relative to m_run)
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_use = 0.f;      // m_run, or 0 while m_run = -inf
+  f32x16 negm = f32x16{}; // splat(-m_use): MFMA accumulator input (prescaled-Q path)
 
   int n_visited = 0, t_first = -1, t_last = -1;  // what the loop walks (tile log)
 
   fetch(0);
-  stash(0);
+  stash(0, 0);
   __syncthreads();
 
   for (int j = 0; j < n_stages; ++j) {
@@ -306,15 +344,23 @@ __global__ __launch_bounds__(R * S * 64) void attn_fwd_kernel(Params p) {
       const u32x4* vt = kt + TILE_CH;
       const int kbase = t * BKV;
 
-      // ---- S^T = K . Q^T ----
+      // ---- S^T = K . Q^T, in exp2 units relative to m_use ----
       f32x16 s[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        s[nb] = f32x16{};
         const int kr = nb * 32 + col;
+        if constexpr (TI::kPrescaleQ) {
+          s[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, half)], qf[0], negm);
+        } else {
+          s[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, half)], qf[0], f32x16{});
+        }
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
+        for (int kk = 1; kk < KSTEPS; ++kk)
           s[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, 2 * kk + half)], qf[kk], s[nb]);
+        if constexpr (!TI::kPrescaleQ) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[nb][i] = __builtin_fmaf(s[nb][i], c, -m_use);
+        }
       }
 
       // ---- mask (boundary tiles only) ----
@@ -329,45 +375,60 @@ __global__ __launch_bounds__(R * S * 64) void attn_fwd_kernel(Params p) {
           }
       }
 
-      // ---- online softmax in exp2 space, lazily rescaled ----
-      float mx = kNegInf;
+      // ---- P = exp2(s), fast path against the current reference max ----
+      u32x4 pb[NG];
+      u32x4 pl[NG];
+      float rs = 0.f;
+      auto make_p = [&](auto shifted, float shift) {
+        rs = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int g16 = 0; g16 < NG; ++g16)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[nb][i], s[nb][i + 1]));
-      mx = fmaxf(mx, other_half(mx)) * c;
-      // Raise the reference max only when some row's tile max exceeds it by
-      // more than 2^kRescale (then P <= 2^kRescale stays well inside fp16).
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescale)) {
-        const float m_new = fmaxf(m_run, mx);
+          for (int w = 0; w < 4; ++w) {
+            const int i = (g16 & 1) * 8 + w * 2;
+            float x0 = s[g16 >> 1][i], x1 = s[g16 >> 1][i + 1];
+            if constexpr (decltype(shifted)::value) { x0 += shift; x1 += shift; }
+            const float p0 = __builtin_amdgcn_exp2f(x0);
+            const float p1 = __builtin_amdgcn_exp2f(x1);
+            const uint32_t hi = TI::pack(p0, p1);
+            pb[g16][w] = hi;
+            if constexpr (TI::kSplitP) {
+              pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
+              rs += p0 + p1;
+            } else {
+              rs = TI::rowsum(hi, rs);
+            }
+          }
+      };
+      bool slow = __builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0;
+      if (!slow) {
+        make_p(std::false_type{}, 0.f);
+        // a p beyond the 16-bit range shows up as inf/NaN in the fp32 row sum
+        slow = __builtin_amdgcn_ballot_w64(!(rs <= 3.0e38f)) != 0;
+      }
+      if (slow) {
+        // exact tile max -> raise the reference, rescale, redo P
+        float mx = kNegInf;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[nb][i], s[nb][i + 1]));
+        mx = fmaxf(mx, other_half(mx));
+        const float mx_abs = mx + m_use;  // -inf stays -inf
+        const float m_new = fmaxf(m_run, mx_abs);
         const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+        const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float shift = m_use - m_use_new;
+        m_use = m_use_new;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+        make_p(std::true_type{}, shift);
       }
-      // all-masked guard: a row that has seen no key keeps m = -inf; its
-      // scores in this tile are all -inf, so subtracting 0 yields p = 0
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-
-      u32x4 pb[NG];
-      u32x4 pl[NG];
-#pragma unroll
-      for (int g16 = 0; g16 < NG; ++g16)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int i = (g16 & 1) * 8 + w * 2;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g16 >> 1][i], c, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g16 >> 1][i + 1], c, -m_use));
-          const uint32_t hi = TI::pack(p0, p1);
-          pb[g16][w] = hi;
-          if constexpr (TI::kSplitP) {
-            pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
-            l_run += p0 + p1;
-          } else {
-            l_run = TI::rowsum(hi, l_run);
-          }
-        }
+      l_run += rs;
 
       // ---- O^T += V^T . P^T ----
 #pragma unroll
@@ -380,7 +441,7 @@ __global__ __launch_bounds__(R * S * 64) void attn_fwd_kernel(Params p) {
         }
     }
 
-    if (j + 1 < n_stages) stash(buf ^ 1);
+    if (j + 1 < n_stages) stash(buf ^ 1, j + 1);
     __syncthreads();
   }
 
