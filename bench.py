@@ -19,7 +19,10 @@ oracle's throughput on a bounded row sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +36,11 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS_F16 = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "prefill attention useful TFLOP/s & % bf16 MFMA peak; us/layer-call at 16k"
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_attention_16k_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "gqa_flash_attention_prefill_amd", "csrc", f)
+                  for f in ("attn_kernel.hip", "attn_internal.h", "attn_api.cpp")]
+COPY_BYTES = 1 << 30   # the calibration copy reads and writes 1 GiB
 
 H_Q, H_KV, D, WINDOW = 64, 8, 64, 128
 LAYERS, CHUNK, TOKENS = 24, 512, 16384
@@ -113,6 +121,114 @@ def cpu_baseline(torch, layers_cpu, budget_s=12.0):
             "seconds": round(s, 2)}
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per full-attention launch from the committed counter summary,
+    or None if it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, read cold: 1 GiB is written, a
+    second 1 GiB buffer is written to push it out of the caches, then the
+    first is copied (1 GiB read + 1 GiB written).  Its FETCH_SIZE /
+    WRITE_SIZE readings scale the attention kernel's counters to bytes."""
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    evict = torch.full((COPY_BYTES // 4,), 2.0, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y, evict
+
+
+def _classify(name):
+    if "attn_fwd_kernel" in name:
+        return "attn_window" if ", true," in name else "attn_full"
+    if "copy" in name.lower() or "elementwise" in name.lower():
+        return "copy"
+    return None
+
+
+def summarize_trace(path):
+    """Average kernel durations from a rocprofv3 --kernel-trace --stats CSV:
+    for each call kind, the instantiation with the most calls (the tuned one;
+    the others ran only in the tuning sweep)."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        kind = _classify(r["Name"])
+        if kind not in ("attn_full", "attn_window"):
+            continue
+        cur = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+               "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+               "kernel": r["Name"]}
+        if kind not in out or cur["calls"] > out[kind]["calls"]:
+            out[kind] = cur
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Per-launch FETCH_SIZE / WRITE_SIZE (KiB) of the full-attention calls and
+    of the calibration copy, and the copy-derived scale factors."""
+    def collect(d, counter):
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                kind = _classify(r["Kernel_Name"])
+                if kind is None:
+                    continue
+                key = (kind, r["Kernel_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        # per kind, keep the instantiation with the most dispatches (the tuned one)
+        by_name = {}
+        for (kind, name, _), v in per.items():
+            by_name.setdefault((kind, name), []).append(v)
+        agg = {}
+        for (kind, name), vals in by_name.items():
+            if kind == "copy":   # the calibration copy is the largest copy dispatch
+                agg["copy"] = [max(agg.get("copy", [0.0]) + vals)]
+            elif kind not in agg or len(vals) > len(agg[kind]):
+                agg[kind] = vals
+        return agg
+    fetch, write = collect(fetch_dir, "FETCH_SIZE"), collect(write_dir, "WRITE_SIZE")
+    copy_f = max(fetch.get("copy", [0.0]))   # the 1 GiB copy is the largest copy dispatch
+    copy_w = max(write.get("copy", [0.0]))
+    kib = COPY_BYTES / 1024.0
+    f_scale = kib / copy_f if copy_f else None
+    w_scale = kib / copy_w if copy_w else None
+    fa = fetch.get("attn_full", [])
+    wa = write.get("attn_full", [])
+    res = {"copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_scale": f_scale,
+           "write_scale": w_scale,
+           "attn_full_launches": len(fa),
+           "attn_full_fetch_kib_raw": sum(fa) / len(fa) if fa else None,
+           "attn_full_write_kib_raw": sum(wa) / len(wa) if wa else None}
+    if fa and wa and f_scale and w_scale:
+        res["fetch_bytes_per_launch"] = res["attn_full_fetch_kib_raw"] * f_scale * 1024
+        res["write_bytes_per_launch"] = res["attn_full_write_kib_raw"] * w_scale * 1024
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,7 +236,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", default=None, help="write per-chunk timings (JSON) here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run the 1 GiB cold copy used to scale HBM counters")
+    ap.add_argument("--summarize-trace", default=None, metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--summarize-counters", nargs=2, default=None,
+                    metavar=("FETCH_SIZE_DIR", "WRITE_SIZE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
+    if args.summarize_counters:
+        res = summarize_counters(*args.summarize_counters)
+        res["kernel_source_sha256"] = kernel_source_hash()
+        print(json.dumps(res, indent=1))
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; a multi-GPU figure is not produced "
               "(run with --gpus 1)", file=sys.stderr)
@@ -200,6 +329,9 @@ def main():
     per_chunk_win = [float(np.mean([mean_call[i] for i in win_idx if calls[i][1] == c])) * 1e3
                      for c in range(N_CHUNKS)]
 
+    if args.copy_calibration:
+        copy_calibration(torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu_layers = []
@@ -243,7 +375,7 @@ def main():
             "peak": PEAK_TFLOPS_F16,
             "unit": "TFLOP/s",
             "frac": round(full_tflops / PEAK_TFLOPS_F16, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "kernel": "full-attention calls (window <= 0)",
         },
         "cpu_baseline": cpu,

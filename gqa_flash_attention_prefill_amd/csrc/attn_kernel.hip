@@ -157,6 +157,10 @@ __device__ inline u32x4 v_frag(const u32x4* vt, int g16, int db, int lane) {
 }
 
 __device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
+
+// s_waitcnt immediate (gfx9 encoding) waiting until at most n vector-memory
+// operations of this wave are outstanding; LDS/export counters unconstrained.
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | (15 << 8) | (7 << 4) | (n & 15); }
 __device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Workgroup = R row groups x S KV splits of one wave each.  Row group rg owns
@@ -174,13 +178,13 @@ __device__ inline float vmax(float a, float b) { return __builtin_elementwise_ma
 //                                                    tiles), its max, the
 //                                                    rescale test
 // so matrix and vector work of neighbouring tiles overlap inside the wave.
-template <int D, int BKV, int R, int S_REQ, bool WIN, typename TI, typename TO>
+template <int D, int BKV, int R, int S_REQ, int NSLOT, bool WIN, typename TI, typename TO>
 __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kernel(Params p) {
-  // three stages of two 64-key d=128 tiles would not fit in LDS: d=128 uses one split
+  // stages of two 64-key d=128 tiles would not fit in LDS: d=128 uses one split
   constexpr int S = (D == 128) ? 1 : S_REQ;
   constexpr int NW = R * S;
   constexpr int NT = NW * 64;
-  constexpr int NSLOT = 3;                  // LDS ring depth (stages)
+  static_assert(NSLOT == 3 || NSLOT == 4, "LDS ring of 3 or 4 stages");
   constexpr int DCH = D / 8;                // 16-byte chunks per K/V row
   constexpr int TILE_CH = BKV * DCH;        // chunks of one K (or V) tile
   constexpr int STAGE_CH = 2 * S * TILE_CH; // K and V of S tiles
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   static_assert(STAGE_CH % (64 * NW) == 0 && TILE_CH % 64 == 0, "direct loads tile the stage");
   auto load_stage = [&](int stage) {
     u32x4* st = lds + (stage % NSLOT) * STAGE_CH;
+    int issued = 0;
 #pragma unroll
     for (int i = 0; i < LD_PER_WAVE; ++i) {
       const int qi = wave * LD_PER_WAVE + i;
@@ -294,6 +299,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
       const int blk = qi % (TILE_CH / 64);
       const int t = t_lo + stage * S + (tt >> 1);
       if (t > t_hi) continue;                  // wave-uniform
+      ++issued;
       const int chunk = blk * 64 + lane;
       const int key = chunk / DCH;
       const int pch = chunk % DCH;
@@ -305,6 +311,15 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
           (const void*)src,
           (__attribute__((address_space(3))) void*)(st + tt * TILE_CH + blk * 64), 16, 0, 0);
     }
+    return issued;
+  };
+  // wait until every stage but the newest one (which issued `newest` loads of
+  // this wave) has landed in LDS
+  auto wait_older = [&](int newest) {
+    if (NSLOT == 4 && newest == LD_PER_WAVE)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LD_PER_WAVE));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
 
   // Running state per row (this lane's query).  m_run is the reference max
@@ -410,7 +425,10 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   // ---- prologue: stages 0 and 1 resident, S of the wave's first tile ----
   load_stage(0);
   if (n_stages > 1) load_stage(1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS loads landed
+  {
+    const int newest = (NSLOT == 4 && n_stages > 2) ? load_stage(2) : 0;
+    wait_older(newest);  // stages 0 and 1 landed
+  }
   __syncthreads();
 
   f32x16 s_a[NB], s_b[NB];   // scores of the current / next tile, roles alternate
@@ -455,7 +473,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   };
 
   auto stage_step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
-    if (j + 2 < n_stages) load_stage(j + 2);
+    const int newest = (j + NSLOT - 1 < n_stages) ? load_stage(j + NSLOT - 1) : 0;
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
       const int ts = t_lo + j * S + s2;
@@ -506,7 +524,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
     cur_ok = nxt_ok;
     t_cur = t_nxt;
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage j + 2 landed in LDS
+    wait_older(newest);  // stage j + 2 landed in LDS
     __syncthreads();
   };
 
@@ -587,495 +605,33 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   }
 }
 
-// ---------------------------------------------------------------------------
-// Wide-wave kernel (d = 64).  Each wave owns 64 Q-tile rows as two 32-row
-// blocks that share every K and V fragment it reads from LDS (half the LDS
-// reads per flop of one 32-row block per wave); one wave per SIMD with the
-// whole register file, which holds the scores of the current and the next
-// tile for the two-phase pipeline described above.  K/V stream into a
-// 3-stage LDS ring with direct global -> LDS loads (global_load_lds_dwordx4:
-// lane i's 16 bytes land at the wave's LDS base + 16 i, so the XOR swizzle
-// is applied by choosing which global chunk each lane fetches).
-// ---------------------------------------------------------------------------
-template <int D, int BKV, int R, int S, bool WIN, typename TI, typename TO>
-__global__ __launch_bounds__(R * S * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_wide(Params p) {
-  constexpr int NW = R * S;
-  constexpr int NSLOT = 3;                  // LDS ring depth (stages)
-  constexpr int NRB = 2;                    // 32-row blocks per wave
-  constexpr int DCH = D / 8;                // 16-byte chunks per K/V row
-  constexpr int TILE_CH = BKV * DCH;        // chunks of one K (or V) tile
-  constexpr int STAGE_CH = 2 * S * TILE_CH; // K and V of S tiles
-  constexpr int LD_PER_WAVE = STAGE_CH / 64 / NW;  // 1-KB direct loads per wave per stage
-  constexpr int KSTEPS = D / 16;
-  constexpr int NB = BKV / 32;
-  constexpr int NG = BKV / 16;
-  constexpr int DB = D / 32;
-  constexpr float kRescale = 8.f;
-  static_assert(D == 64 && DCH == 8, "wide kernel: d = 64 (one 128-byte row per key)");
-  static_assert(STAGE_CH % (64 * NW) == 0 && TILE_CH % 64 == 0, "direct loads tile the stage");
-  static_assert(S == 1 || S == 2, "1 or 2 KV splits");
-
-  __shared__ u32x4 lds[NSLOT * STAGE_CH];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rg = wave % R;
-  const int sp = wave / R;
-  const int half = lane >> 5;
-  const int col = lane & 31;
-
-  // ---- work item: (KV head, head group, Q tile), heaviest Q tiles first ----
-  const int item = blockIdx.x;
-  const int g = item % p.h_kv;
-  const int r0 = item / p.h_kv;
-  const int hg = r0 % p.n_hgroups;
-  const int tix = p.seq.cu_tiles[p.seq.n_seq] - 1 - r0 / p.n_hgroups;
-  int bi = 0;
-  {
-    int lo = 0, hi = p.seq.n_seq - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.seq.cu_tiles[mid] <= tix) lo = mid; else hi = mid - 1;
-    }
-    bi = lo;
-  }
-  const int sq = p.seq.cu_q[bi + 1] - p.seq.cu_q[bi];
-  const int past = p.seq.past[bi];
-  const int slot = p.seq.slot[bi];
-  const int64_t tok0 = p.seq.cu_q[bi];
-  const int q0 = (tix - p.seq.cu_tiles[bi]) * p.q_rows;
-  const int q_last = min(q0 + p.q_rows, sq) - 1;
-  const int skv = past + sq;
-  const int window = WIN ? p.window : 0;
-
-  const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
-  const int t_lo = lo_key / BKV;
-  const int t_hi = (past + q_last) / BKV;
-  const int n_stages = (t_hi - t_lo + S) / S;
-
-  // ---- this lane's two rows (one per row block) ----
-  int pos[NRB], head[NRB], row_hi[NRB], row_lo[NRB];
-  bool valid[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int row = rg * 64 + rb * 32 + col;
-    pos[rb] = q0 + row / p.hpack;
-    head[rb] = g * p.group + hg * p.hpack + row % p.hpack;
-    valid[rb] = pos[rb] < sq;
-    row_hi[rb] = past + pos[rb];
-    row_lo[rb] = window > 0 ? past + pos[rb] - window + 1 : 0;
-  }
-  const int wp0 = q0 + (rg * 64) / p.hpack;
-  const int wp1 = min(q0 + (rg * 64 + 63) / p.hpack, sq - 1);
-  const bool wave_live = wp0 < sq;
-  const int w_lo = window > 0 ? max(0, past + wp0 - window + 1) / BKV : 0;
-  const int w_hi = (past + wp1) / BKV;
-  const int w_full_lo = window > 0 ? past + wp1 - window + 1 : 0;
-  const int w_full_hi = past + wp0;
-
-  const float c = p.scale_log2;
-  const float kNegInf = -__builtin_inff();
-
-  u32x4 qf[NRB][KSTEPS];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int64_t qoff = ((tok0 + pos[rb]) * p.h_q + head[rb]) * D + half * 8;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const u32x4 v = valid[rb] ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
-      if constexpr (TI::kPrescaleQ) {
-        const f16x8 h8 = __builtin_bit_cast(f16x8, v);
-        f16x8 o8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = (_Float16)((float)h8[e] * c);
-        qf[rb][kk] = __builtin_bit_cast(u32x4, o8);
-      } else {
-        qf[rb][kk] = v;
-      }
-    }
-  }
-
-  const int64_t kv_base = ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
-  const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
-  const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
-
-  // ---- direct global -> LDS load of one stage ----
-  // The stage is 2S tile-tensors ((split, K|V)) of TILE_CH 16-byte chunks;
-  // wave w issues 1-KB loads q = w * LD_PER_WAVE + i.  Lane l of a load
-  // fills LDS chunk 64 * block + l of its tile-tensor: key 8 * block + l / 8,
-  // physical chunk l % 8, i.e. logical chunk (l % 8) ^ swizzle(key).  Rows
-  // at or past skv are read from row skv - 1 (finite data; the causal mask
-  // gives those keys p = 0).
-  const int key_in_blk = lane >> 3;
-  const int pchunk = lane & 7;
-  auto load_stage = [&](int stage) {
-    u32x4* st = lds + (stage % NSLOT) * STAGE_CH;
-#pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) {
-      const int qi = wave * LD_PER_WAVE + i;
-      const int tt = qi / (TILE_CH / 64);      // tile-tensor: 2 * split + (0 K, 1 V)
-      const int blk = qi % (TILE_CH / 64);
-      const int t = t_lo + stage * S + (tt >> 1);
-      if (t > t_hi) continue;                  // wave-uniform
-      const int key = blk * 8 + key_in_blk;
-      const int row = min(t * BKV + key, skv - 1);
-      const bool is_v = tt & 1;
-      const int ch = is_v ? v_chunk(key, pchunk) : k_chunk(key, pchunk);
-      const uint16_t* src = (is_v ? vptr : kptr) + (int64_t)row * D + ch * 8;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)(st + tt * TILE_CH + blk * 64), 16, 0, 0);
-    }
-  };
-
-  float m_run[NRB], l_run[NRB], m_use[NRB];
-  f32x16 negm[NRB];
-  f32x16 acc[NRB][DB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_run[rb] = 0.f;
-    m_use[rb] = 0.f;
-    negm[rb] = f32x16{};
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x16{};
-  }
-
-  auto wave_tile = [&](int j, int* t) {
-    *t = t_lo + j * S + sp;
-    return wave_live && j < n_stages && *t <= t_hi && *t >= w_lo && *t <= w_hi;
-  };
-  auto scores = [&](const u32x4* kt, f32x16 (*sc)[NB]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int kr = nb * 32 + col;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const u32x4 a = kt[kr * DCH + k_chunk(kr, 2 * kk + half)];
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          if (kk == 0) {
-            if constexpr (TI::kPrescaleQ) sc[rb][nb] = TI::mma(a, qf[rb][0], negm[rb]);
-            else sc[rb][nb] = TI::mma(a, qf[rb][0], f32x16{});
-          } else {
-            sc[rb][nb] = TI::mma(a, qf[rb][kk], sc[rb][nb]);
-          }
-        }
-      }
-    }
-  };
-  auto to_exp2_units = [&](f32x16 (*sc)[NB]) {
-    if constexpr (!TI::kPrescaleQ) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[rb][nb][i] = __builtin_fmaf(sc[rb][nb][i], c, -m_use[rb]);
-    }
-  };
-  auto row_max = [&](const f32x16* sc) {
-    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2)
-        m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[nb][i], sc[nb][i + 1]));
-    const float mx = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]));
-    return vmax(mx, other_half(mx));
-  };
-  auto interior = [&](int t) {
-    const int kbase = t * BKV;
-    return (kbase + BKV - 1 <= w_full_hi) && (kbase >= w_full_lo);
-  };
-  auto apply_mask = [&](int t, f32x16 (*sc)[NB]) {
-    const int kbase = t * BKV;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + nb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key > row_hi[rb] || key < row_lo[rb]) sc[rb][nb][i] = kNegInf;
-        }
-  };
-  auto rebase = [&](const float* mx, f32x16 (*sc)[NB]) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const bool need = (mx[rb] > kRescale) || (m_run[rb] == kNegInf && mx[rb] != kNegInf);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float mx_abs = mx[rb] + m_use[rb];
-        const float m_new = fmaxf(m_run[rb], mx_abs);
-        const float alpha =
-            (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[rb][db] *= alpha;
-        m_run[rb] = m_new;
-        const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
-        const float shift = m_use[rb] - m_use_new;
-        m_use[rb] = m_use_new;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) negm[rb][i] = -m_use_new;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[rb][nb][i] += shift;
-      }
-    }
-  };
-  auto make_p = [&](f32x16 (*s_cur)[NB], u32x4 (*pb)[NG], u32x4 (*pl)[NG]) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      float rs = 0.f;
-#pragma unroll
-      for (int g16 = 0; g16 < NG; ++g16)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int i = (g16 & 1) * 8 + w * 2;
-          const float p0 = __builtin_amdgcn_exp2f(s_cur[rb][g16 >> 1][i]);
-          const float p1 = __builtin_amdgcn_exp2f(s_cur[rb][g16 >> 1][i + 1]);
-          const uint32_t hi = TI::pack(p0, p1);
-          pb[rb][g16][w] = hi;
-          if constexpr (TI::kSplitP) {
-            pl[rb][g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
-            rs += p0 + p1;
-          } else {
-            rs = TI::rowsum(hi, rs);
-          }
-        }
-      l_run[rb] += rs;
-    }
-  };
-  auto pv = [&](const u32x4* vt, u32x4 (*pb)[NG], u32x4 (*pl)[NG]) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g16 = 0; g16 < NG; ++g16) {
-        const u32x4 a = v_frag<D>(vt, g16, db, lane);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          acc[rb][db] = TI::mma(a, pb[rb][g16], acc[rb][db]);
-          if constexpr (TI::kSplitP) acc[rb][db] = TI::mma(a, pl[rb][g16], acc[rb][db]);
-        }
-      }
-  };
-
-  int n_visited = 0, t_first = -1, t_last = -1;
-
-  // ---- prologue: stages 0 and 1 resident, scores of the wave's first tile ----
-  load_stage(0);
-  if (n_stages > 1) load_stage(1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS loads landed
-  __syncthreads();
-
-  f32x16 s_a[NRB][NB], s_b[NRB][NB];
-  int t_cur = 0;
-  bool cur_ok = wave_tile(0, &t_cur);
-  if (cur_ok) {
-    scores(lds + (2 * sp) * TILE_CH, s_a);
-    to_exp2_units(s_a);
-    if (!interior(t_cur)) apply_mask(t_cur, s_a);
-    float mx[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) mx[rb] = row_max(s_a[rb]);
-    rebase(mx, s_a);
-  }
-
-  auto stage_step = [&](int j, f32x16 (*s_cur)[NB], f32x16 (*s_nxt)[NB]) {
-    if (j + 2 < n_stages) load_stage(j + 2);
-#pragma unroll
-    for (int s2 = 0; s2 < S; ++s2) {
-      const int ts = t_lo + j * S + s2;
-      if (ts <= t_hi) {
-        if (t_first < 0) t_first = ts;
-        t_last = ts;
-        ++n_visited;
-      }
-    }
-    int t_nxt = 0;
-    const bool nxt_ok = wave_tile(j + 1, &t_nxt);
-    const u32x4* k_cur_slot = lds + (j % NSLOT) * STAGE_CH + (2 * sp) * TILE_CH;
-    const u32x4* k_nxt_slot = lds + ((j + 1) % NSLOT) * STAGE_CH + (2 * sp) * TILE_CH;
-    const u32x4* vt = k_cur_slot + TILE_CH;
-    u32x4 pb[NRB][NG];
-    u32x4 pl[NRB][NG];
-    float mx[NRB] = {kNegInf, kNegInf};
-
-    if (cur_ok && nxt_ok) {
-      scores(k_nxt_slot, s_nxt);
-      make_p(s_cur, pb, pl);
-      pv(vt, pb, pl);
-      to_exp2_units(s_nxt);
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) mx[rb] = row_max(s_nxt[rb]);
-    } else {
-      if (nxt_ok) scores(k_nxt_slot, s_nxt);
-      if (cur_ok) {
-        make_p(s_cur, pb, pl);
-        pv(vt, pb, pl);
-      }
-      if (nxt_ok) {
-        to_exp2_units(s_nxt);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) mx[rb] = row_max(s_nxt[rb]);
-      }
-    }
-    if (nxt_ok) {
-      if (!interior(t_nxt)) {
-        apply_mask(t_nxt, s_nxt);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) mx[rb] = row_max(s_nxt[rb]);
-      }
-      rebase(mx, s_nxt);
-    }
-    cur_ok = nxt_ok;
-    t_cur = t_nxt;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // stage j + 2 landed in LDS
-    __syncthreads();
-  };
-
-  for (int j = 0; j < n_stages; j += 2) {
-    stage_step(j, s_a, s_b);
-    if (j + 1 < n_stages) stage_step(j + 1, s_b, s_a);
-  }
-
-  // ---- merge the KV splits of each row group through LDS ----
-  if constexpr (S > 1) {
-    constexpr int NV = NRB * (2 + 16 * DB);
-    float* mb = reinterpret_cast<float*>(lds);
-    if (sp == 1) {
-      float* dst = mb + rg * NV * 64 + lane;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        float* d2 = dst + rb * (2 + 16 * DB) * 64;
-        d2[0] = m_run[rb];
-        d2[64] = l_run[rb];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) d2[(2 + db * 16 + i) * 64] = acc[rb][db][i];
-      }
-    }
-    __syncthreads();
-    if (sp == 0) {
-      const float* src = mb + rg * NV * 64 + lane;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float* s2 = src + rb * (2 + 16 * DB) * 64;
-        const float m1 = s2[0], l1 = s2[64];
-        const float m = fmaxf(m_run[rb], m1);
-        const float a0 = (m_run[rb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - m);
-        const float a1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-        l_run[rb] = a0 * l_run[rb] + a1 * l1;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            acc[rb][db][i] = a0 * acc[rb][db][i] + a1 * s2[(2 + db * 16 + i) * 64];
-        m_run[rb] = m;
-      }
-    }
-  }
-
-  // ---- epilogue ----
-  if (sp == 0) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      float l_tot = l_run[rb] + other_half(l_run[rb]);
-      if (p.sink != nullptr && m_run[rb] != kNegInf)
-        l_tot += __builtin_amdgcn_exp2f(p.sink[head[rb]] * kLog2e - m_run[rb]);
-      const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
-      if (valid[rb]) {
-        const int64_t ooff = ((tok0 + pos[rb]) * p.h_q + head[rb]) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int d0 = db * 32 + i4 * 8 + half * 4;
-            const float o0 = acc[rb][db][i4 * 4 + 0] * inv, o1 = acc[rb][db][i4 * 4 + 1] * inv;
-            const float o2 = acc[rb][db][i4 * 4 + 2] * inv, o3 = acc[rb][db][i4 * 4 + 3] * inv;
-            if constexpr (sizeof(TO) == 4) {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
-                  f32x4{o0, o1, o2, o3};
-            } else {
-              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
-                  u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
-            }
-          }
-      }
-    }
-  }
-
-  if (p.log != nullptr && tid == 0) {
-    int32_t* rec = p.log + (int64_t)blockIdx.x * 8;
-    rec[0] = slot;
-    rec[1] = g * p.group + hg * p.hpack;
-    rec[2] = p.hpack;
-    rec[3] = q0;
-    rec[4] = q_last;
-    rec[5] = t_first;
-    rec[6] = t_last;
-    rec[7] = n_visited;
-  }
-}
-
-template <int D, int BKV, int R, int S, typename TI, typename TO>
-hipError_t launch_wide(const Params& p, int n_items, hipStream_t stream) {
-  if (p.window > 0)
-    hipLaunchKernelGGL((attn_fwd_wide<D, BKV, R, S, true, TI, TO>), dim3(n_items),
-                       dim3(R * S * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_wide<D, BKV, R, S, false, TI, TO>), dim3(n_items),
-                       dim3(R * S * 64), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <int D, int BKV, int R, int S, typename TI, typename TO>
+template <int D, int BKV, int R, int S, int NS, typename TI, typename TO>
 hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
   constexpr int threads = R * (D == 128 ? 1 : S) * 64;
   if (p.window > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, true, TI, TO>), dim3(n_items),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, true, TI, TO>), dim3(n_items),
                        dim3(threads), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, false, TI, TO>), dim3(n_items),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, false, TI, TO>), dim3(n_items),
                        dim3(threads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int BKV, int R, int S>
+template <int BKV, int R, int S, int NS = 3>
 constexpr KernelConfig make_config(const char* name) {
   return KernelConfig{
       name, BKV, R * 32,
-      {{{launch<64, BKV, R, S, F16, uint16_t>, launch<64, BKV, R, S, F16, float>},
-        {launch<64, BKV, R, S, BF16, uint16_t>, launch<64, BKV, R, S, BF16, float>}},
-       {{launch<128, BKV, R, S, F16, uint16_t>, launch<128, BKV, R, S, F16, float>},
-        {launch<128, BKV, R, S, BF16, uint16_t>, launch<128, BKV, R, S, BF16, float>}}}};
-}
-
-// fp16 d = 64 on the wide-wave kernel (2 row groups of 64 rows); bf16 (two
-// PV products per step, whose extra registers the wide kernel cannot hold)
-// and d = 128 on the 32-row-per-wave kernel (4 row groups).  All give
-// 128-row Q tiles.
-template <int BKV, int S>
-constexpr KernelConfig make_wide_config(const char* name) {
-  return KernelConfig{
-      name, BKV, 128,
-      {{{launch_wide<64, BKV, 2, S, F16, uint16_t>, launch_wide<64, BKV, 2, S, F16, float>},
-        {launch<64, BKV, 4, S, BF16, uint16_t>, launch<64, BKV, 4, S, BF16, float>}},
-       {{launch<128, BKV, 4, S, F16, uint16_t>, launch<128, BKV, 4, S, F16, float>},
-        {launch<128, BKV, 4, S, BF16, uint16_t>, launch<128, BKV, 4, S, BF16, float>}}}};
+      {{{launch<64, BKV, R, S, NS, F16, uint16_t>, launch<64, BKV, R, S, NS, F16, float>},
+        {launch<64, BKV, R, S, NS, BF16, uint16_t>, launch<64, BKV, R, S, NS, BF16, float>}},
+       {{launch<128, BKV, R, S, NS, F16, uint16_t>, launch<128, BKV, R, S, NS, F16, float>},
+        {launch<128, BKV, R, S, NS, BF16, uint16_t>, launch<128, BKV, R, S, NS, BF16, float>}}}};
 }
 
 const KernelConfig kConfigs[] = {
-    make_wide_config<64, 2>("r128_kv64_w2"),
+    make_config<64, 4, 2, 4>("r128_kv64_s2_ring4"),
     make_config<64, 4, 2>("r128_kv64_s2"),
     make_config<64, 4, 1>("r128_kv64_s1"),
     make_config<32, 2, 2>("r64_kv32_s2"),
-    make_config<64, 2, 2>("r64_kv64_s2"),
 };
 
 }  // namespace
