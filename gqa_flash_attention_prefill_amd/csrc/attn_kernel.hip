@@ -158,6 +158,24 @@ __device__ inline u32x4 v_frag(const u32x4* vt, int g16, int db, int lane) {
 
 __device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
 
+// One 16-byte-per-lane direct global -> LDS load (global_load_lds_dwordx4):
+// lane i reads sbase + voff and its 16 bytes land at LDS byte address
+// lds_addr + 16 i.  Issued through inline assembly so that the compiler does
+// not treat it as an LDS store that every later LDS read must wait for (the
+// loads fill a ring slot that no wave reads until the stage barrier; the
+// kernel waits for them with explicit s_waitcnt vmcnt before that barrier).
+__device__ inline void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // s_waitcnt immediate (gfx9 encoding) waiting until at most n vector-memory
 // operations of this wave are outstanding; LDS/export counters unconstrained.
 constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | (15 << 8) | (7 << 4) | (n & 15); }
@@ -200,7 +218,9 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep every
+  // quantity derived from it in scalar registers and branch on it with SALU
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave % R;
   const int sp = wave / R;
   const int half = lane >> 5;
@@ -289,6 +309,21 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   // skv - 1 (finite data whose scores the causal mask removes, p = 0).
   constexpr int LD_PER_WAVE = STAGE_CH / 64 / NW;
   static_assert(STAGE_CH % (64 * NW) == 0 && TILE_CH % 64 == 0, "direct loads tile the stage");
+  // this lane's key and byte offset inside its tile for each of the wave's
+  // loads (the same every stage)
+  int ld_key[LD_PER_WAVE];
+  uint32_t ld_off[LD_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < LD_PER_WAVE; ++i) {
+    const int qi = wave * LD_PER_WAVE + i;
+    const int tt = qi / (TILE_CH / 64);
+    const int chunk = (qi % (TILE_CH / 64)) * 64 + lane;
+    const int key = chunk / DCH;
+    const int pch = chunk % DCH;
+    const int ch = (tt & 1) ? v_chunk(key, pch) : k_chunk(key, pch);
+    ld_key[i] = key;
+    ld_off[i] = (uint32_t)(key * D + ch * 8) * 2u;
+  }
   auto load_stage = [&](int stage) {
     u32x4* st = lds + (stage % NSLOT) * STAGE_CH;
     int issued = 0;
@@ -300,16 +335,15 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
       const int t = t_lo + stage * S + (tt >> 1);
       if (t > t_hi) continue;                  // wave-uniform
       ++issued;
-      const int chunk = blk * 64 + lane;
-      const int key = chunk / DCH;
-      const int pch = chunk % DCH;
-      const int row = min(t * BKV + key, skv - 1);
-      const bool is_v = tt & 1;
-      const int ch = is_v ? v_chunk(key, pch) : k_chunk(key, pch);
-      const uint16_t* src = (is_v ? vptr : kptr) + (int64_t)row * D + ch * 8;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)(st + tt * TILE_CH + blk * 64), 16, 0, 0);
+      const char* tile = reinterpret_cast<const char*>((tt & 1) ? vptr : kptr) +
+                         (int64_t)t * (BKV * D * 2);
+      uint32_t voff = ld_off[i];
+      if (t * BKV + BKV > skv) {
+        // the tile that crosses the end of the sequence: clamp rows to skv - 1
+        const int row = min(ld_key[i], skv - 1 - t * BKV);
+        voff -= (uint32_t)(ld_key[i] - row) * (D * 2);
+      }
+      lds_dma16(tile, voff, lds_byte_addr(st + tt * TILE_CH + blk * 64));
     }
     return issued;
   };
@@ -396,6 +430,12 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
     if (!interior(t)) apply_mask(t, sc);
     return row_max(sc);
   };
+  auto set_neg_inf = [&](f32x16* sc) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[nb][i] = kNegInf;
+  };
   // raise the reference max if the tile needs it (wave-uniform branch);
   // acc must not have pending PV work of an older tile when this runs
   auto rebase = [&](float mx, f32x16* sc) {
@@ -433,14 +473,15 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
 
   f32x16 s_a[NB], s_b[NB];   // scores of the current / next tile, roles alternate
   int t_cur = 0;
-  bool cur_ok = wave_tile(0, &t_cur);
-  if (cur_ok) {
+  if (wave_tile(0, &t_cur)) {
     scores(lds + (2 * sp) * TILE_CH, t_cur, s_a);
     const float mx = prepare(t_cur, s_a);
     rebase(mx, s_a);
+  } else {
+    set_neg_inf(s_a);
   }
 
-  // P = exp2(S) of the current tile, 16-bit, with this lane's row sums
+  // P = exp2(S) of the current tile, 16-bit; returns this lane's row sum
   auto make_p = [&](const f32x16* s_cur, u32x4* pb, u32x4* pl) {
     float rs = 0.f;
 #pragma unroll
@@ -459,7 +500,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
           rs = TI::rowsum(hi, rs);
         }
       }
-    l_run += rs;
+    return rs;
   };
   auto pv = [&](const u32x4* vt, const u32x4* pb, const u32x4* pl) {
 #pragma unroll
@@ -489,30 +530,20 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
     const u32x4* k_cur_slot = lds + (j % NSLOT) * STAGE_CH + (2 * sp) * TILE_CH;
     const u32x4* k_nxt_slot = lds + ((j + 1) % NSLOT) * STAGE_CH + (2 * sp) * TILE_CH;
     const u32x4* vt = k_cur_slot + TILE_CH;
+    // One straight-line body for every stage (no branch on whether this wave
+    // has a current or a next tile), so that the scheduler can interleave
+    //   S_{i+1} (MFMA) || P_i (VALU);  PV_i (MFMA) || max of S_{i+1} (VALU)
+    // and the accumulators keep one register assignment.  Without a next
+    // tile the scores come from a resident (stale) slot and are replaced by
+    // -inf, so that the following stage's P is exactly zero and its PV and
+    // row sum add nothing.
     u32x4 pb[NG];
     u32x4 pl[NG];
-    float mx = kNegInf;
-
-    if (cur_ok && nxt_ok) {
-      // steady state, one straight-line block so that the scheduler can
-      // interleave the two MFMA groups with the vector work:
-      //   S_{i+1} (MFMA) || P_i (VALU);  PV_i (MFMA) || raw max of S_{i+1} (VALU)
-      scores(k_nxt_slot, t_nxt, s_nxt);
-      make_p(s_cur, pb, pl);
-      pv(vt, pb, pl);
-      to_exp2_units(s_nxt);
-      mx = row_max(s_nxt);
-    } else {
-      if (nxt_ok) scores(k_nxt_slot, t_nxt, s_nxt);
-      if (cur_ok) {
-        make_p(s_cur, pb, pl);
-        pv(vt, pb, pl);
-      }
-      if (nxt_ok) {
-        to_exp2_units(s_nxt);
-        mx = row_max(s_nxt);
-      }
-    }
+    scores(k_nxt_slot, t_nxt, s_nxt);
+    l_run += make_p(s_cur, pb, pl);
+    pv(vt, pb, pl);
+    to_exp2_units(s_nxt);
+    float mx = row_max(s_nxt);
     if (nxt_ok) {
       // boundary tile: mask, then the max of what is kept (rare)
       if (!interior(t_nxt)) {
@@ -520,9 +551,9 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
         mx = row_max(s_nxt);
       }
       rebase(mx, s_nxt);
+    } else {
+      set_neg_inf(s_nxt);
     }
-    cur_ok = nxt_ok;
-    t_cur = t_nxt;
 
     wait_older(newest);  // stage j + 2 landed in LDS
     __syncthreads();
