@@ -291,7 +291,7 @@ int run(const Call& c) {
       return fail(ATTN_EINVAL, "tile log holds %lld records, %lld needed",
                   (long long)c.log->capacity, (long long)need);
     log_base = c.log->records;
-    c.log->bkv = attn::config(cfg).bkv;
+    c.log->bkv = attn::config(cfg).bkv[c.d == 128];
     const int hpack = gcd_int(c.h_q / c.h_kv, 32);
     c.log->q_rows = attn::config(cfg).rows / hpack;
   }

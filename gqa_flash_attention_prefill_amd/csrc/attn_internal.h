@@ -42,7 +42,7 @@ using LaunchFn = hipError_t (*)(const Params&, int n_items, hipStream_t);
 
 struct KernelConfig {
   const char* name;
-  int bkv;        // keys per KV tile
+  int bkv[2];     // keys per KV tile, [d == 128]
   int rows;       // Q-tile rows (q positions x packed heads)
   // indexed [d == 128][dtype == bf16][out is f32]
   LaunchFn fn[2][2][2];

@@ -67,6 +67,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct F16 {
   static constexpr bool kSplitP = false;
+  static constexpr uint32_t kOnePair = 0x3c003c00u;  // two fp16 1.0
   // Q is pre-scaled by scale * log2(e) (one extra fp16 rounding of q, ~1e-4
   // relative in p, the size of P's own rounding) so that S^T arrives in exp2
   // units and the running max can enter through the MFMA accumulator input.
@@ -90,6 +91,7 @@ struct F16 {
 
 struct BF16 {
   static constexpr bool kSplitP = true;
+  static constexpr uint32_t kOnePair = 0x3f803f80u;  // two bf16 1.0
   static constexpr bool kPrescaleQ = false;  // a bf16 rounding of q*c would cost ~1e-3
   __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -117,13 +119,26 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // 16-byte-chunk XOR swizzles of the K and V tiles in LDS (both row-major,
-// one key per row).
-//  K: S^T reads 16 bytes per lane with lanes 0..7 on keys 0..7 of one chunk
-//     column -> chunk ^ (key & 7) spreads them over 8 distinct chunks.
-//  V: transposed reads (ds_read_b64_tr_b16) take 4 keys x 32 bytes per 16-lane
-//     group -> pair-of-chunks ^ (key & 3) puts the 4 keys on distinct banks.
-__device__ inline int k_chunk(int key, int c) { return c ^ (key & 7); }
-__device__ inline int v_chunk(int key, int c) { return c ^ ((key & 3) << 1); }
+// one key per row), chosen so that the fragment reads below are free of bank
+// conflicts on the 64-bank (256 B per clock) LDS:
+//  K: S^T reads 16 bytes per lane, lanes 0..15 on 16 consecutive keys of one
+//     chunk column; a pass serves 16 lanes = 256 bytes, so the 16 keys must
+//     land on 16 distinct 16-byte bank groups.  At d = 64 a key row is half
+//     the bank width: keys 2i and 2i + 1 sit in opposite halves, and
+//     chunk ^ ((key >> 1) & 7) spreads each half's 8 keys over its 8 groups.
+//     At d = 128 a row spans all banks: chunk ^ (key & 15).
+//  V: transposed reads (ds_read_b64_tr_b16) take 4 keys x 32 bytes per
+//     16-lane group and 8 keys per instruction; chunk ^ ((key & 3) << 1) at
+//     d = 64 and chunk ^ ((key & 3) << 2) at d = 128 give every key of an
+//     instruction its own banks.
+template <int D>
+__device__ inline int k_chunk(int key, int c) {
+  return D == 64 ? c ^ ((key >> 1) & 7) : c ^ (key & 15);
+}
+template <int D>
+__device__ inline int v_chunk(int key, int c) {
+  return D == 64 ? c ^ ((key & 3) << 1) : c ^ ((key & 3) << 2);
+}
 
 // Lane layout used with v_mfma_f32_32x32x16 (A: 32 rows x 16 k, B: 16 k x 32
 // cols, C: 32 x 32):  A/B lane l holds row/col l % 32 and k = 8 (l / 32) + 0..7;
@@ -148,8 +163,8 @@ __device__ inline u32x4 v_frag(const u32x4* vt, int g16, int db, int lane) {
   const int key_a = g16 * 16 + 4 * h + (j >> 2);
   const int key_b = key_a + 8;
   const uint16_t* base = reinterpret_cast<const uint16_t*>(vt);
-  const uint16_t* pa = base + (key_a * DCH + v_chunk(key_a, d >> 3)) * 8 + (d & 7);
-  const uint16_t* pb = base + (key_b * DCH + v_chunk(key_b, d >> 3)) * 8 + (d & 7);
+  const uint16_t* pa = base + (key_a * DCH + v_chunk<D>(key_a, d >> 3)) * 8 + (d & 7);
+  const uint16_t* pb = base + (key_b * DCH + v_chunk<D>(key_b, d >> 3)) * 8 + (d & 7);
   const s16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
   const s16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pb);
   const u32x2 a2 = __builtin_bit_cast(u32x2, ra), b2 = __builtin_bit_cast(u32x2, rb);
@@ -157,6 +172,17 @@ __device__ inline u32x4 v_frag(const u32x4* vt, int g16, int db, int lane) {
 }
 
 __device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
+
+// max(x, x of lane ^ 32) through v_permlane32_swap (a VALU lane swap between
+// the two 32-lane halves; no LDS round trip).  With both operands holding x,
+// the swap leaves the low half's values in one register and the high half's
+// in the other, in every lane.  The s_nop covers the VALU-write ->
+// permlane-read hazard of the operands.
+__device__ inline float pair_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return __builtin_elementwise_maximum(a, b);
+}
 
 // One 16-byte-per-lane direct global -> LDS load (global_load_lds_dwordx4):
 // lane i reads sbase + voff and its 16 bytes land at LDS byte address
@@ -320,21 +346,22 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
     const int chunk = (qi % (TILE_CH / 64)) * 64 + lane;
     const int key = chunk / DCH;
     const int pch = chunk % DCH;
-    const int ch = (tt & 1) ? v_chunk(key, pch) : k_chunk(key, pch);
+    const int ch = (tt & 1) ? v_chunk<D>(key, pch) : k_chunk<D>(key, pch);
     ld_key[i] = key;
     ld_off[i] = (uint32_t)(key * D + ch * 8) * 2u;
   }
+  // A split whose tile lies past t_hi in the last stage gets tile t_hi
+  // instead: every slot a wave reads then holds finite cache data, which
+  // matters because a wave without a tile still multiplies P = 0 by V.
+  const uint32_t lds_addr = lds_byte_addr(lds);
   auto load_stage = [&](int stage) {
-    u32x4* st = lds + (stage % NSLOT) * STAGE_CH;
-    int issued = 0;
+    const uint32_t st = lds_addr + (uint32_t)((stage % NSLOT) * STAGE_CH) * 16u;
 #pragma unroll
     for (int i = 0; i < LD_PER_WAVE; ++i) {
       const int qi = wave * LD_PER_WAVE + i;
       const int tt = qi / (TILE_CH / 64);      // tile-tensor: 2 * split + (0 K, 1 V)
       const int blk = qi % (TILE_CH / 64);
-      const int t = t_lo + stage * S + (tt >> 1);
-      if (t > t_hi) continue;                  // wave-uniform
-      ++issued;
+      const int t = min(t_lo + stage * S + (tt >> 1), t_hi);
       const char* tile = reinterpret_cast<const char*>((tt & 1) ? vptr : kptr) +
                          (int64_t)t * (BKV * D * 2);
       uint32_t voff = ld_off[i];
@@ -343,14 +370,13 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
         const int row = min(ld_key[i], skv - 1 - t * BKV);
         voff -= (uint32_t)(ld_key[i] - row) * (D * 2);
       }
-      lds_dma16(tile, voff, lds_byte_addr(st + tt * TILE_CH + blk * 64));
+      lds_dma16(tile, voff, st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
     }
-    return issued;
   };
-  // wait until every stage but the newest one (which issued `newest` loads of
-  // this wave) has landed in LDS
-  auto wait_older = [&](int newest) {
-    if (NSLOT == 4 && newest == LD_PER_WAVE)
+  // wait until every stage but the newest one has landed in LDS (`newest`:
+  // whether a newer stage's loads were issued after it)
+  auto wait_older = [&](bool newest) {
+    if (NSLOT == 4 && newest)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(LD_PER_WAVE));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -380,12 +406,12 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
     for (int nb = 0; nb < NB; ++nb) {
       const int kr = nb * 32 + col;
       if constexpr (TI::kPrescaleQ)
-        sc[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, half)], qf[0], negm);
+        sc[nb] = TI::mma(kt[kr * DCH + k_chunk<D>(kr, half)], qf[0], negm);
       else
-        sc[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, half)], qf[0], f32x16{});
+        sc[nb] = TI::mma(kt[kr * DCH + k_chunk<D>(kr, half)], qf[0], f32x16{});
 #pragma unroll
       for (int kk = 1; kk < KSTEPS; ++kk)
-        sc[nb] = TI::mma(kt[kr * DCH + k_chunk(kr, 2 * kk + half)], qf[kk], sc[nb]);
+        sc[nb] = TI::mma(kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)], qf[kk], sc[nb]);
     }
   };
   // bf16 path: scores to exp2 units relative to m_use (fp16 path: already)
@@ -406,8 +432,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
 #pragma unroll
       for (int i = 0; i < 16; i += 2)
         m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[nb][i], sc[nb][i + 1]));
-    const float mx = vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]));
-    return vmax(mx, other_half(mx));
+    return pair_max(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])));
   };
   // is tile t free of masked (row, key) pairs for every row of this wave?
   auto interior = [&](int t) {
@@ -466,7 +491,8 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   load_stage(0);
   if (n_stages > 1) load_stage(1);
   {
-    const int newest = (NSLOT == 4 && n_stages > 2) ? load_stage(2) : 0;
+    const bool newest = NSLOT == 4 && n_stages > 2;
+    if (newest) load_stage(2);
     wait_older(newest);  // stages 0 and 1 landed
   }
   __syncthreads();
@@ -514,7 +540,8 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   };
 
   auto stage_step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
-    const int newest = (j + NSLOT - 1 < n_stages) ? load_stage(j + NSLOT - 1) : 0;
+    const bool newest = j + NSLOT - 1 < n_stages;
+    if (newest) load_stage(j + NSLOT - 1);
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
       const int ts = t_lo + j * S + s2;
@@ -636,6 +663,476 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant: 8 waves = 2 groups x 4 row groups.  Group g (= KV split
+// g) takes tiles t_lo + 2 j + g.  Each wave alternates two phases separated
+// by workgroup barriers:
+//   M_j  matrix work only:  S_{j+1} = K_{j+1} . Q^T  and  O^T += V_j^T . P_j^T
+//        from fragments already in registers;
+//   V_j  vector work only:  mask / max / lazy rescale of S_{j+1}, P_{j+1} =
+//        exp2(S_{j+1}) packed to 16 bits, row sums; the direct loads of tile
+//        j + NS; the LDS reads of the K_{j+2} and V_{j+1} fragments.
+// Group 1 starts one phase late, so on every SIMD (one wave of each group)
+// one wave's MFMA burst runs beside the other wave's exp2 / VALU burst.
+// Each group owns an NS-slot ring of (K, V) tiles in LDS, filled by its own
+// four waves.
+template <int D, int BKV_REQ, int NS_REQ, bool WIN, typename TI, typename TO>
+__global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
+  constexpr int BKV = (D == 128) ? 32 : BKV_REQ;  // ring of 2 x NS tiles must fit LDS
+  constexpr int NS = (D == 128) ? 4 : NS_REQ;      // (a 5-deep ring spills at d = 128)
+  constexpr int R = 4;                      // row groups (waves) per group
+  constexpr int DCH = D / 8;
+  constexpr int TILE_CH = BKV * DCH;        // 16-byte chunks of one K (or V) tile
+  constexpr int SLOT_CH = 2 * TILE_CH;      // K and V of one tile
+  constexpr int GROUP_CH = NS * SLOT_CH;    // one group's ring
+  constexpr int KSTEPS = D / 16;
+  constexpr int NB = BKV / 32;
+  constexpr int NG = BKV / 16;
+  constexpr int DB = D / 32;
+  constexpr int LPW = SLOT_CH / 64 / R;     // 1-KB direct loads per wave per tile
+  constexpr float kRescale = 8.f;
+  static_assert(NS == 4 || NS == 5, "ring of 4 or 5 tiles per group");
+  static_assert(SLOT_CH % (64 * R) == 0, "direct loads tile a slot");
+  static_assert(2 * GROUP_CH * 16 <= 160 * 1024, "LDS");
+
+  __shared__ u32x4 lds[2 * GROUP_CH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % R;
+  const int grp = wave / R;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // ---- work item: (KV head, head group, Q tile), heaviest Q tiles first ----
+  const int item = blockIdx.x;
+  const int g = item % p.h_kv;
+  const int r0 = item / p.h_kv;
+  const int hg = r0 % p.n_hgroups;
+  const int tix = p.seq.cu_tiles[p.seq.n_seq] - 1 - r0 / p.n_hgroups;
+  int bi = 0;
+  {
+    int lo = 0, hi = p.seq.n_seq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq.cu_tiles[mid] <= tix) lo = mid; else hi = mid - 1;
+    }
+    bi = lo;
+  }
+  const int sq = p.seq.cu_q[bi + 1] - p.seq.cu_q[bi];
+  const int past = p.seq.past[bi];
+  const int slot = p.seq.slot[bi];
+  const int64_t tok0 = p.seq.cu_q[bi];
+  const int q0 = (tix - p.seq.cu_tiles[bi]) * p.q_rows;
+  const int q_last = min(q0 + p.q_rows, sq) - 1;
+  const int skv = past + sq;
+  const int window = WIN ? p.window : 0;
+
+  const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
+  const int t_lo = lo_key / BKV;
+  const int t_hi = (past + q_last) / BKV;
+  const int n_stages = (t_hi - t_lo + 2) / 2;  // tiles of group 0 (group 1: same or one fewer)
+
+  const int row = rg * 32 + col;
+  const int pos = q0 + row / p.hpack;
+  const int head = g * p.group + hg * p.hpack + row % p.hpack;
+  const bool valid = pos < sq;
+  const int row_hi = past + pos;
+  const int row_lo = window > 0 ? past + pos - window + 1 : 0;
+
+  const int wp0 = q0 + (rg * 32) / p.hpack;
+  const int wp1 = min(q0 + (rg * 32 + 31) / p.hpack, sq - 1);
+  const bool wave_live = wp0 < sq;
+  const int w_lo = window > 0 ? max(0, past + wp0 - window + 1) / BKV : 0;
+  const int w_hi = (past + wp1) / BKV;
+  const int w_full_lo = window > 0 ? past + wp1 - window + 1 : 0;
+  const int w_full_hi = past + wp0;
+
+  const float c = p.scale_log2;
+  const float kNegInf = -__builtin_inff();
+
+  u32x4 qf[KSTEPS];
+  {
+    const int64_t qoff = ((tok0 + pos) * p.h_q + head) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const u32x4 v = valid ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
+      if constexpr (TI::kPrescaleQ) {
+        const f16x8 h8 = __builtin_bit_cast(f16x8, v);
+        f16x8 o8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = (_Float16)((float)h8[e] * c);
+        qf[kk] = __builtin_bit_cast(u32x4, o8);
+      } else {
+        qf[kk] = v;
+      }
+    }
+  }
+
+  const int64_t kv_base = ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
+  const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
+  const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
+  u32x4* const ring = lds + grp * GROUP_CH;
+  // LDS byte address of the ring (cast once: the generic -> LDS cast carries
+  // a null check that per-load casts would repeat)
+  const uint32_t ring_addr = lds_byte_addr(ring);
+
+  // ---- direct loads of one tile of this group: wave rg issues loads
+  // rg * LPW + i of the slot's 2 * TILE_CH / 64 one-KB pieces (K then V) ----
+  int ld_key[LPW];
+  uint32_t ld_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int qi = rg * LPW + i;
+    const int tt = qi / (TILE_CH / 64);
+    const int chunk = (qi % (TILE_CH / 64)) * 64 + lane;
+    const int key = chunk / DCH;
+    const int pch = chunk % DCH;
+    const int ch = tt ? v_chunk<D>(key, pch) : k_chunk<D>(key, pch);
+    ld_key[i] = key;
+    ld_off[i] = (uint32_t)(key * D + ch * 8) * 2u;
+  }
+  // A group-local index past the group's last tile loads tile t_hi instead,
+  // so every slot a wave reads holds finite cache data (a wave without a
+  // tile still multiplies P = 0 by its V fragments).
+  auto load_tile = [&](int j) {
+    const int t = min(t_lo + 2 * j + grp, t_hi);
+    const uint32_t st = ring_addr + (uint32_t)((j % NS) * SLOT_CH) * 16u;
+    const bool tail = t * BKV + BKV > skv;  // the tile that crosses the end of the keys
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int qi = rg * LPW + i;
+      const int tt = qi / (TILE_CH / 64);
+      const int blk = qi % (TILE_CH / 64);
+      const char* tile = reinterpret_cast<const char*>(tt ? vptr : kptr) + (int64_t)t * (BKV * D * 2);
+      uint32_t voff = ld_off[i];
+      if (tail) {
+        const int r = min(ld_key[i], skv - 1 - t * BKV);
+        voff -= (uint32_t)(ld_key[i] - r) * (D * 2);
+      }
+      lds_dma16(tile, voff, st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
+    }
+  };
+
+  auto wave_tile = [&](int j, int* t) {
+    *t = t_lo + 2 * j + grp;
+    return wave_live && j >= 0 && j < n_stages && *t <= t_hi && *t >= w_lo && *t <= w_hi;
+  };
+
+  float m_run = kNegInf, m_use = 0.f;
+  f32x16 negm = f32x16{};
+  // Row sums of P on the matrix pipe: ones . P^T puts the sum of P over the
+  // tile's keys in every element of the row's column (the vector pipe is the
+  // busier one at d = 64).
+  f32x16 lsum = f32x16{};
+  const u32x4 ones = {TI::kOnePair, TI::kOnePair, TI::kOnePair, TI::kOnePair};
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  f32x16 sc[NB];
+  u32x4 kf[NB][KSTEPS];
+  u32x4 vf[DB][NG];
+  u32x4 pb[NG], pl[NG];
+#pragma unroll
+  for (int g16 = 0; g16 < NG; ++g16) {
+    pb[g16] = u32x4{0, 0, 0, 0};
+    pl[g16] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vf[db][g16] = u32x4{0, 0, 0, 0};
+  }
+
+  auto read_k = [&](int j) {
+    const u32x4* kt = ring + (j % NS) * SLOT_CH;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int kr = nb * 32 + col;
+        kf[nb][kk] = kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)];
+      }
+  };
+  auto read_v = [&](int j) {
+    const u32x4* vt = ring + (j % NS) * SLOT_CH + TILE_CH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g16 = 0; g16 < NG; ++g16) vf[db][g16] = v_frag<D>(vt, g16, db, lane);
+  };
+  // M_j: S_{j+1} = K_{j+1} . Q^T from kf and O^T += V_j^T . P_j^T from vf,
+  // refilling each fragment register from the next tile (kf <- K_{j+2},
+  // vf <- V_{j+1}) right after the MFMA that last reads it.  One or two LDS
+  // reads between consecutive MFMAs keep this wave's issue slots busy while
+  // the matrix pipe runs, without the read bursts that overflow the LDS
+  // command queue (four waves of a CU are in this phase at once).
+  auto m_phase = [&](int j) {
+    const u32x4* kt = ring + ((j + 2) % NS) * SLOT_CH;
+    const u32x4* vt = ring + ((j + 1) % NS) * SLOT_CH + TILE_CH;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (kk == 0)
+          sc[nb] = TI::mma(kf[nb][0], qf[0], TI::kPrescaleQ ? negm : f32x16{});
+        else
+          sc[nb] = TI::mma(kf[nb][kk], qf[kk], sc[nb]);
+        const int kr = nb * 32 + col;
+        kf[nb][kk] = kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)];
+      }
+#pragma unroll
+    for (int g16 = 0; g16 < NG; ++g16) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc[db] = TI::mma(vf[db][g16], pb[g16], acc[db]);
+        if constexpr (TI::kSplitP) acc[db] = TI::mma(vf[db][g16], pl[g16], acc[db]);
+        vf[db][g16] = v_frag<D>(vt, g16, db, lane);
+      }
+      lsum = TI::mma(ones, pb[g16], lsum);
+      if constexpr (TI::kSplitP) lsum = TI::mma(ones, pl[g16], lsum);
+    }
+    // issue order: (MFMA, read) x NB*KSTEPS, then per 16-key step
+    // (MFMA, 2 reads) x DB and the row-sum MFMA
+    constexpr int kMfma = 0x008, kDsRead = 0x100;
+#pragma unroll
+    for (int i = 0; i < NB * KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int g16 = 0; g16 < NG; ++g16) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, TI::kSplitP ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kMfma, TI::kSplitP ? 2 : 1, 0);
+    }
+  };
+  auto make_p = [&]() {
+#pragma unroll
+    for (int g16 = 0; g16 < NG; ++g16)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int i = (g16 & 1) * 8 + w * 2;
+        const float p0 = __builtin_amdgcn_exp2f(sc[g16 >> 1][i]);
+        const float p1 = __builtin_amdgcn_exp2f(sc[g16 >> 1][i + 1]);
+        const uint32_t hi = TI::pack(p0, p1);
+        pb[g16][w] = hi;
+        if constexpr (TI::kSplitP)
+          pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
+      }
+  };
+  // in-lane part of the row max (the other 16 keys of each row are in lane ^ 32)
+  auto lane_max = [&]() {
+    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[nb][i], sc[nb][i + 1]));
+    return vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]));
+  };
+  auto apply_mask = [&](int t) {
+    const int kbase = t * BKV;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kbase + nb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+        if (key > row_hi || key < row_lo) sc[nb][i] = kNegInf;
+      }
+  };
+
+  // One V phase: softmax of S_{j+1} into P_{j+1}.  P is formed against the
+  // current reference max first; only when some row's max moved past the
+  // threshold (rare: early tiles, rising scores) is the reference raised,
+  // O and l rescaled and P formed again.
+  auto v_phase = [&](int j) {
+    int t = 0;
+    const bool ok = wave_tile(j + 1, &t);
+    if (ok) {
+      if constexpr (!TI::kPrescaleQ) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[nb][i] = __builtin_fmaf(sc[nb][i], c, -m_use);
+      }
+      if (!((t * BKV + BKV - 1 <= w_full_hi) && (t * BKV >= w_full_lo))) apply_mask(t);
+      const float mx = pair_max(lane_max());
+      make_p();
+      const bool need = (mx > kRescale) || (m_run == kNegInf && mx != kNegInf);
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mx_abs = mx + m_use;
+        const float m_new = fmaxf(m_run, mx_abs);
+        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+        const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float shift = m_use - m_use_new;
+        m_use = m_use_new;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[nb][i] += shift;
+        make_p();
+      }
+    } else {
+#pragma unroll
+      for (int g16 = 0; g16 < NG; ++g16) {
+        pb[g16] = u32x4{0, 0, 0, 0};
+        pl[g16] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Tile t is read by M_{t-2} (K fragments) and M_{t-1} (V fragments).  Its
+  // direct loads are issued in M_{t-NS+1} (the prologue for t < NS - 1) into
+  // the slot of tile t - NS, whose last reader M_{t-NS-1} finished before the
+  // barrier that opened V_{t-NS-1}.  The end of V_j waits for tile j + 3;
+  // later tiles may still be in flight.
+  auto wait_tiles = [&](int j) {
+    const int newest = min(j + NS - 1, n_stages - 1);  // last tile requested so far
+    const int ahead = newest - (j + 3);                 // tiles allowed in flight
+    if (NS == 5 && ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
+    else if (ahead >= 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+
+  // ---- prologue: tiles 0 .. NS-2 requested, 0 and 1 landed ----
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_stages) load_tile(j);
+  {
+    const int newest = min(NS - 2, n_stages - 1);
+    if (newest - 1 >= 2 && NS == 5)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
+    else if (newest - 1 >= 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  barrier();
+  read_k(0);
+  if (grp == 1) barrier();  // group 1 runs one phase behind group 0
+
+  for (int j = -1; j < n_stages; ++j) {
+    // ---- M_j ----
+    __builtin_amdgcn_s_setprio(1);
+    if (j >= 0 && j + NS - 1 < n_stages) load_tile(j + NS - 1);
+    m_phase(j);
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+    // ---- V_j ----
+    v_phase(j);
+    wait_tiles(j);
+    barrier();
+  }
+  // what the loop walked: group-local stages 0 .. n_stages - 1, tiles
+  // t_lo + 2 j + {0, 1} up to t_hi
+  const int n_visited = n_stages > 0 ? t_hi - t_lo + 1 : 0;
+  const int t_first = n_stages > 0 ? t_lo : -1;
+  const int t_last = n_stages > 0 ? t_hi : -1;
+  // the last prefetch reads must be done before LDS is reused for the merge
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  if (grp == 0) barrier();
+
+  float l_run = lsum[0];  // the row's full sum (both lane halves' keys)
+  // ---- merge the two groups' partial (m, l, O) through LDS ----
+  {
+    constexpr int NV = 2 + 16 * DB;
+    float* mb = reinterpret_cast<float*>(lds);
+    if (grp == 1) {
+      float* dst = mb + rg * NV * 64 + lane;
+      dst[0] = m_run;
+      dst[64] = l_run;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(2 + db * 16 + i) * 64] = acc[db][i];
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float* src = mb + rg * NV * 64 + lane;
+      const float m1 = src[0], l1 = src[64];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[db][i] = a0 * acc[db][i] + a1 * src[(2 + db * 16 + i) * 64];
+      m_run = m;
+    }
+  }
+
+  if (grp == 0) {
+    float l_tot = l_run;
+    if (p.sink != nullptr && m_run != kNegInf) {
+      const float sk = p.sink[head];
+      l_tot += __builtin_amdgcn_exp2f(sk * kLog2e - m_run);
+    }
+    const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
+    if (valid) {
+      const int64_t ooff = ((tok0 + pos) * p.h_q + head) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = db * 32 + i4 * 8 + half * 4;
+          const float o0 = acc[db][i4 * 4 + 0] * inv, o1 = acc[db][i4 * 4 + 1] * inv;
+          const float o2 = acc[db][i4 * 4 + 2] * inv, o3 = acc[db][i4 * 4 + 3] * inv;
+          if constexpr (sizeof(TO) == 4) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
+                f32x4{o0, o1, o2, o3};
+          } else {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
+                u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
+          }
+        }
+    }
+  }
+
+  if (p.log != nullptr && tid == 0) {
+    int32_t* rec = p.log + (int64_t)blockIdx.x * 8;
+    rec[0] = slot;
+    rec[1] = g * p.group + hg * p.hpack;
+    rec[2] = p.hpack;
+    rec[3] = q0;
+    rec[4] = q_last;
+    rec[5] = t_first;
+    rec[6] = t_last;
+    rec[7] = n_visited;
+  }
+}
+
+template <int D, int BKV, int NS, typename TI, typename TO>
+hipError_t launch_pp(const Params& p, int n_items, hipStream_t stream) {
+  if (p.window > 0)
+    hipLaunchKernelGGL((attn_pp_kernel<D, BKV, NS, true, TI, TO>), dim3(n_items), dim3(512), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((attn_pp_kernel<D, BKV, NS, false, TI, TO>), dim3(n_items), dim3(512), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+
 template <int D, int BKV, int R, int S, int NS, typename TI, typename TO>
 hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
   constexpr int threads = R * (D == 128 ? 1 : S) * 64;
@@ -651,14 +1148,28 @@ hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
 template <int BKV, int R, int S, int NS = 3>
 constexpr KernelConfig make_config(const char* name) {
   return KernelConfig{
-      name, BKV, R * 32,
+      name, {BKV, BKV}, R * 32,
       {{{launch<64, BKV, R, S, NS, F16, uint16_t>, launch<64, BKV, R, S, NS, F16, float>},
         {launch<64, BKV, R, S, NS, BF16, uint16_t>, launch<64, BKV, R, S, NS, BF16, float>}},
        {{launch<128, BKV, R, S, NS, F16, uint16_t>, launch<128, BKV, R, S, NS, F16, float>},
         {launch<128, BKV, R, S, NS, BF16, uint16_t>, launch<128, BKV, R, S, NS, BF16, float>}}}};
 }
 
+// Ping-pong configuration for d = 64; at d = 128 (where its register budget
+// does not hold two groups' fragments) the same entry runs the split-free
+// kernel with the same 128-row Q tiles.
+template <int BKV, int NS>
+constexpr KernelConfig make_pp_config(const char* name) {
+  return KernelConfig{
+      name, {BKV, 64}, 128,
+      {{{launch_pp<64, BKV, NS, F16, uint16_t>, launch_pp<64, BKV, NS, F16, float>},
+        {launch_pp<64, BKV, NS, BF16, uint16_t>, launch_pp<64, BKV, NS, BF16, float>}},
+       {{launch<128, 64, 4, 1, 3, F16, uint16_t>, launch<128, 64, 4, 1, 3, F16, float>},
+        {launch<128, 64, 4, 1, 3, BF16, uint16_t>, launch<128, 64, 4, 1, 3, BF16, float>}}}};
+}
+
 const KernelConfig kConfigs[] = {
+    make_pp_config<64, 4>("pp_r128_kv64_ring4"),
     make_config<64, 4, 2, 4>("r128_kv64_s2_ring4"),
     make_config<64, 4, 2>("r128_kv64_s2"),
     make_config<64, 4, 1>("r128_kv64_s1"),
