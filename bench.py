@@ -295,8 +295,12 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done; tuning: {binding.attn_tune_stats()}", file=sys.stderr,
-          flush=True)
+    tuned = {}
+    for kind, w in (("full", -1), ("window", WINDOW)):
+        idx = binding.attn_tuned_config(D, torch.float16, torch.float16, CHUNK, H_Q, H_KV, w, 1)
+        tuned[kind] = binding.attn_config_name(idx) if idx >= 0 else None
+    print(f"[bench] warmup done; tuning: {binding.attn_tune_stats()}; chosen: {tuned}",
+          file=sys.stderr, flush=True)
 
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in calls] for _ in range(args.steps)]
@@ -368,6 +372,7 @@ def main():
             "us_per_layer_call": round(1e3 * (full_ms + win_ms) / len(calls), 2),
             "attn_ms_per_16k_prefill": round(full_ms + win_ms, 3),
             "frac_peak_whole_step": round(value / PEAK_TFLOPS_F16, 4),
+            "kernel_config": tuned,
         },
         "roofline": {
             "bound": "mfma",

@@ -23,7 +23,8 @@ LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last
 _DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
 
 EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_last_error", "attn_tune_stats",
-            "attn_tune_reset", "attn_config_count", "attn_config_name", "attn_force_config")
+            "attn_tune_reset", "attn_tuned_config", "attn_config_count", "attn_config_name",
+            "attn_force_config")
 
 
 class AttnError(RuntimeError):
@@ -71,6 +72,8 @@ def lib():
     L.attn_tune_stats.restype = ctypes.c_int
     L.attn_tune_reset.argtypes = []
     L.attn_tune_reset.restype = None
+    L.attn_tuned_config.argtypes = [_i32, _i32, _i32, ctypes.c_int64, _i32, _i32, _i32, _i32]
+    L.attn_tuned_config.restype = ctypes.c_int32
     L.attn_config_count.argtypes = []
     L.attn_config_count.restype = ctypes.c_int32
     L.attn_config_name.argtypes = [_i32]
@@ -173,6 +176,13 @@ def attn_tune_stats():
 
 def attn_tune_reset():
     lib().attn_tune_reset()
+
+
+def attn_tuned_config(d, dtype, out_dtype, q_tokens, h_q, h_kv, window, batch):
+    """Index of the configuration the tuning cache chose for this call key, or -1.
+    dtype / out_dtype are torch dtypes."""
+    return lib().attn_tuned_config(d, _DTYPE_CODE[dtype], _DTYPE_CODE[out_dtype], q_tokens, h_q,
+                                   h_kv, window, batch)
 
 
 def attn_config_count():

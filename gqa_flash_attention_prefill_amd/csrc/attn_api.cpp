@@ -169,9 +169,24 @@ int64_t plan_items(const Call& c, int cfg_index) {
   return tiles * c.h_kv * (group / hpack);
 }
 
+// The key leaves out the KV depth, so its one sweep stands for every depth
+// the key will see (for a chunked prefill: the first, shallowest chunk would
+// be a poor sample).  The sweep therefore times each sequence at depth
+// max(past, min(s_cap, kSweepDepth) - sq): deeper keys of the caller's own
+// cache (rows past the valid prefix are in bounds; what they hold only
+// reaches the sweep's discarded output).
+constexpr int32_t kSweepDepth = 16384;
+
 // One synchronous sweep: time each configuration on the caller's buffers and
 // stream (the output is overwritten by the real launch that follows).
-int sweep(const Call& c, int* best_out) {
+int sweep(const Call& c_in, int* best_out) {
+  std::vector<int32_t> deep(c_in.batch > 0 ? c_in.batch : 1);
+  for (int32_t b = 0; b < c_in.batch; ++b) {
+    const int32_t sq = c_in.cu[b + 1] - c_in.cu[b];
+    deep[b] = std::max(c_in.past[b], std::min(c_in.s_cap, kSweepDepth) - sq);
+  }
+  Call c = c_in;
+  c.past = deep.data();
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
     return fail(ATTN_EHIP, "hipEventCreate failed");
@@ -355,6 +370,16 @@ void attn_tune_reset(void) {
   g_tune.clear();
   g_sweeps = 0;
   g_tune_launches = 0;
+}
+
+int32_t attn_tuned_config(int32_t d, int32_t dtype, int32_t out_dtype, int64_t q_tokens,
+                          int32_t h_q, int32_t h_kv, int32_t window, int32_t batch) {
+  if (h_kv <= 0) return -1;
+  const TuneKey key{d, dtype, out_dtype, q_tokens, h_q, h_q / h_kv, window > 0 ? window : 0,
+                    batch, 0};
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  auto it = g_tune.find(key);
+  return it == g_tune.end() ? -1 : it->second;
 }
 
 int32_t attn_config_count(void) { return attn::config_count(); }

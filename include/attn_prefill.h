@@ -139,11 +139,18 @@ const char* attn_last_error(void);
  * tokens of the call, h_q, group size, window, batch).  The first call for a
  * key times every kernel configuration once (a synchronous sweep on the
  * caller's stream, without the sink) and keeps the fastest; later calls with
- * the same key reuse it.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and
- * uses the default configuration; ATTN_PREFILL_CONFIG=<name> forces one.
+ * the same key reuse it.  Since the key leaves out the KV depth, the sweep
+ * times every sequence at depth max(past_len, min(s_cap, 16384) - sq) of the
+ * caller's cache, so that the choice made on a shallow first chunk holds for
+ * the deep ones.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and uses the
+ * default configuration; ATTN_PREFILL_CONFIG=<name> forces one.
  */
 int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys);
 void attn_tune_reset(void);
+/* The configuration index the tuning cache holds for a key (the arguments of
+ * a call: q_tokens = rows of q), or -1 if that key has not been swept. */
+int32_t attn_tuned_config(int32_t d, int32_t dtype, int32_t out_dtype, int64_t q_tokens,
+                          int32_t h_q, int32_t h_kv, int32_t window, int32_t batch);
 
 /* Kernel configurations: count, name of index i (NULL if out of range), and
  * forcing one for all later calls of this process (index -1 clears). */

@@ -41,6 +41,12 @@ def test_one_sweep_per_layer_type_over_a_chunked_prefill(monkeypatch):
     assert st["tuning_launches"] == 2 * n_cfg * 4, st
     for _, _, out in layers:
         assert torch.isfinite(out).all()
+    # the cache answers for exactly the two swept keys
+    for window in (-1, 128):
+        idx = binding.attn_tuned_config(64, torch.float16, torch.float16, chunk, 16, 2, window, 1)
+        assert 0 <= idx < n_cfg
+    assert binding.attn_tuned_config(64, torch.float16, torch.float16, chunk, 16, 2, 64, 1) == -1
+    assert binding.attn_tuned_config(64, torch.float16, torch.float16, chunk + 1, 16, 2, -1, 1) == -1
 
 
 def test_disabled_tuning_uses_default_without_sweeping(monkeypatch):
