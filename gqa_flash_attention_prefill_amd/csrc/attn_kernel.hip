@@ -692,6 +692,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   constexpr int LPW = SLOT_CH / 64 / R;     // 1-KB direct loads per wave per tile
   constexpr float kRescale = 8.f;
   static_assert(NS == 4 || NS == 5, "ring of 4 or 5 tiles per group");
+  static_assert(NB <= 2, "one -m splat per 32-key block (negm, negm1)");
   static_assert(SLOT_CH % (64 * R) == 0, "direct loads tile a slot");
   static_assert(2 * GROUP_CH * 16 <= 160 * 1024, "LDS");
 
@@ -821,7 +822,11 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   };
 
   float m_run = kNegInf, m_use = 0.f;
+  // splat(-m_use), the accumulator input of the first S MFMA of each 32-key
+  // block; one copy per block, since an MFMA that reads its accumulator
+  // input in place would otherwise make the compiler copy it every phase
   f32x16 negm = f32x16{};
+  f32x16 negm1 = f32x16{};
   // Row sums of P on the matrix pipe: ones . P^T puts the sum of P over the
   // tile's keys in every element of the row's column (the vector pipe is the
   // busier one at d = 64).
@@ -873,7 +878,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         if (kk == 0)
-          sc[nb] = TI::mma(kf[nb][0], qf[0], TI::kPrescaleQ ? negm : f32x16{});
+          sc[nb] = TI::mma(kf[nb][0], qf[0], TI::kPrescaleQ ? (nb ? negm1 : negm) : f32x16{});
         else
           sc[nb] = TI::mma(kf[nb][kk], qf[kk], sc[nb]);
         const int kr = nb * 32 + col;
@@ -974,6 +979,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         m_use = m_use_new;
 #pragma unroll
         for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+        negm1 = negm;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1032,8 +1038,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   for (int j = -1; j < n_stages; ++j) {
     // ---- M_j ----
     __builtin_amdgcn_s_setprio(1);
-    if (j >= 0 && j + NS - 1 < n_stages) load_tile(j + NS - 1);
     m_phase(j);
+    // the direct loads go after the MFMAs: issued while the last ones drain
+    __builtin_amdgcn_sched_barrier(0);
+    if (j >= 0 && j + NS - 1 < n_stages) load_tile(j + NS - 1);
     __builtin_amdgcn_s_setprio(0);
     barrier();
     // ---- V_j ----
