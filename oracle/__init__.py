@@ -10,6 +10,8 @@ All arrays are numpy float64 (exact copies of the fp16/bf16 inputs); layouts:
   q, out      [tokens, h_q, d]          (tokens = cu_seqlens_q[-1])
   k, v        [batch, h_kv, s_cap, d]
   sink        [h_q] or None
+  lse         [tokens, h_q]             (natural log of the sum of exp over
+                                         the row's kept scores; sink excluded)
 """
 import ctypes
 import os
@@ -40,10 +42,18 @@ def _load():
         _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _dp,
         ctypes.c_double, _dp, _i32]
     lib.oracle_attn_prefill_varlen.restype = ctypes.c_int
+    lib.oracle_attn_prefill_varlen_lse.argtypes = [
+        _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _dp,
+        ctypes.c_double, _dp, _dp, _i32]
+    lib.oracle_attn_prefill_varlen_lse.restype = ctypes.c_int
     lib.oracle_attn_rows.argtypes = [
         _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _dp,
         ctypes.c_double, _i64, _i64p, _i32p, _dp, _i32]
     lib.oracle_attn_rows.restype = ctypes.c_int
+    lib.oracle_attn_rows_lse.argtypes = [
+        _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _dp,
+        ctypes.c_double, _i64, _i64p, _i32p, _dp, _dp, _i32]
+    lib.oracle_attn_rows_lse.restype = ctypes.c_int
     lib.oracle_attn_masked.argtypes = [
         _dp, _dp, _dp, _i32, _i32, _i32, _u8p, ctypes.c_double, ctypes.c_double, _dp]
     lib.oracle_attn_masked.restype = ctypes.c_int
@@ -69,8 +79,10 @@ def _i32arr(a):
     return a, a.ctypes.data_as(_i32p)
 
 
-def attn_prefill_varlen(q, k, v, cu_seqlens_q, past_len, window, sink, scale, threads=0):
-    """Full output [tokens, h_q, d] in float64 (see attn_oracle.c)."""
+def attn_prefill_varlen(q, k, v, cu_seqlens_q, past_len, window, sink, scale, threads=0,
+                        return_lse=False):
+    """Full output [tokens, h_q, d] in float64 (see attn_oracle.c); with
+    return_lse, also the log-sum-exp [tokens, h_q] of each row's kept scores."""
     lib = _load()
     q, qp = _f64(q)
     k, kp = _f64(k)
@@ -86,15 +98,18 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, past_len, window, sink, scale, th
     else:
         sp = None
     out = np.zeros((tokens, h_q, d), dtype=np.float64)
-    rc = lib.oracle_attn_prefill_varlen(qp, kp, vp, batch, cup, plp, h_q, h_kv, d, s_cap,
-                                        int(window), sp, float(scale),
-                                        out.ctypes.data_as(_dp), int(threads))
+    lse = np.zeros((tokens, h_q), dtype=np.float64) if return_lse else None
+    rc = lib.oracle_attn_prefill_varlen_lse(qp, kp, vp, batch, cup, plp, h_q, h_kv, d, s_cap,
+                                            int(window), sp, float(scale),
+                                            out.ctypes.data_as(_dp),
+                                            lse.ctypes.data_as(_dp) if return_lse else None,
+                                            int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attn_prefill_varlen rejected its arguments ({rc})")
-    return out
+    return (out, lse) if return_lse else out
 
 
-def attn_prefill(q, k, v, past_len, window, sink, scale, threads=0):
+def attn_prefill(q, k, v, past_len, window, sink, scale, threads=0, return_lse=False):
     """One sequence: q [sq, h_q, d], k/v [1, h_kv, s_cap, d] (or [h_kv, s_cap, d])."""
     k = np.asarray(k)
     v = np.asarray(v)
@@ -102,12 +117,14 @@ def attn_prefill(q, k, v, past_len, window, sink, scale, threads=0):
         k = k[None]
         v = v[None]
     sq = q.shape[0]
-    return attn_prefill_varlen(q, k, v, [0, sq], [past_len], window, sink, scale, threads)
+    return attn_prefill_varlen(q, k, v, [0, sq], [past_len], window, sink, scale, threads,
+                               return_lse)
 
 
 def attn_rows(q, k, v, cu_seqlens_q, past_len, window, sink, scale, row_tok, row_head,
-              threads=0):
-    """Output rows [(row_tok[r], row_head[r])] -> array [n_rows, d] in float64."""
+              threads=0, return_lse=False):
+    """Output rows [(row_tok[r], row_head[r])] -> array [n_rows, d] in float64
+    (and, with return_lse, their log-sum-exp [n_rows])."""
     lib = _load()
     q, qp = _f64(q)
     k, kp = _f64(k)
@@ -124,12 +141,14 @@ def attn_rows(q, k, v, cu_seqlens_q, past_len, window, sink, scale, row_tok, row
     else:
         sp = None
     out = np.zeros((rt.shape[0], d), dtype=np.float64)
-    rc = lib.oracle_attn_rows(qp, kp, vp, batch, cup, plp, h_q, h_kv, d, s_cap, int(window),
-                              sp, float(scale), rt.shape[0], rt.ctypes.data_as(_i64p),
-                              rh.ctypes.data_as(_i32p), out.ctypes.data_as(_dp), int(threads))
+    lse = np.zeros(rt.shape[0], dtype=np.float64) if return_lse else None
+    rc = lib.oracle_attn_rows_lse(qp, kp, vp, batch, cup, plp, h_q, h_kv, d, s_cap, int(window),
+                                  sp, float(scale), rt.shape[0], rt.ctypes.data_as(_i64p),
+                                  rh.ctypes.data_as(_i32p), out.ctypes.data_as(_dp),
+                                  lse.ctypes.data_as(_dp) if return_lse else None, int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attn_rows rejected its arguments ({rc})")
-    return out
+    return (out, lse) if return_lse else out
 
 
 def attn_masked(q, k, v, mask, sink, scale):

@@ -86,7 +86,7 @@ int oracle_kept(int64_t past_len, int64_t q, int64_t k, int64_t window)
  * ------------------------------------------------------------------------- */
 static void attend_row(const double* q_row, const double* k_head, const double* v_head,
                        int64_t d, int64_t skv, int64_t past_len, int64_t q, int64_t window,
-                       double sink, double scale, double* score, double* out)
+                       double sink, double scale, double* score, double* out, double* lse)
 {
     int64_t j, t;
     int any = 0;
@@ -101,6 +101,22 @@ static void attend_row(const double* q_row, const double* k_head, const double* 
         any = 1;
     }
     for (t = 0; t < d; ++t) out[t] = 0.0;
+    /* 1b. optional log-sum-exp of the kept scores, natural log, sink left
+     *     out: lse = log(sum_j exp(S_j)) over kept j, written as
+     *     max + log(sum_j exp(S_j - max)); -inf for a row with no kept key.
+     *     This is the quantity partial results over disjoint key ranges are
+     *     merged with (sglang's "lse_extend" side output). */
+    if (lse) {
+        double mk = -INFINITY, sum = 0.0;
+        for (j = 0; j < skv; ++j) if (score[j] > mk) mk = score[j];
+        if (mk == -INFINITY) {
+            *lse = -INFINITY;
+        } else {
+            for (j = 0; j < skv; ++j)
+                if (score[j] != -INFINITY) sum += exp(score[j] - mk);
+            *lse = mk + log(sum);
+        }
+    }
     /* 2. a row with no kept key: output 0, sink not added */
     if (!any) return;
 
@@ -146,11 +162,11 @@ static int check_batch(int32_t batch, const int32_t* cu_seqlens_q, const int32_t
  *   nthreads     : OpenMP threads (<= 0: the runtime default)
  * Returns 0, or -2 on an invalid argument.
  * ------------------------------------------------------------------------- */
-int oracle_attn_prefill_varlen(const double* q, const double* k, const double* v,
-                               int32_t batch, const int32_t* cu_seqlens_q, const int32_t* past_len,
-                               int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
-                               int32_t window, const double* sink, double scale,
-                               double* out, int32_t nthreads)
+int oracle_attn_prefill_varlen_lse(const double* q, const double* k, const double* v,
+                                   int32_t batch, const int32_t* cu_seqlens_q,
+                                   const int32_t* past_len, int32_t h_q, int32_t h_kv, int32_t d,
+                                   int32_t s_cap, int32_t window, const double* sink,
+                                   double scale, double* out, double* lse, int32_t nthreads)
 {
     int64_t n_units, u;
     int32_t group;
@@ -175,7 +191,8 @@ int oracle_attn_prefill_varlen(const double* q, const double* k, const double* v
         for (i = 0; i < sq; ++i) {
             int64_t tok = cu_seqlens_q[b] + i;
             attend_row(q + (tok * h_q + h) * d, kh, vh, d, skv, past_len[b], i, window, s,
-                       scale, score, out + (tok * h_q + h) * d);
+                       scale, score, out + (tok * h_q + h) * d,
+                       lse ? lse + tok * h_q + h : NULL);
         }
         free(score);
     }
@@ -183,17 +200,28 @@ int oracle_attn_prefill_varlen(const double* q, const double* k, const double* v
     return 0;
 }
 
+/* The same without the log-sum-exp output. */
+int oracle_attn_prefill_varlen(const double* q, const double* k, const double* v,
+                               int32_t batch, const int32_t* cu_seqlens_q, const int32_t* past_len,
+                               int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                               int32_t window, const double* sink, double scale,
+                               double* out, int32_t nthreads)
+{
+    return oracle_attn_prefill_varlen_lse(q, k, v, batch, cu_seqlens_q, past_len, h_q, h_kv, d,
+                                          s_cap, window, sink, scale, out, NULL, nthreads);
+}
+
 /* ---------------------------------------------------------------------------
  * Selected rows only, for spot checks at sizes where the full oracle is too
  * slow.  Row r is (token row_tok[r], q head row_head[r]); its output goes to
  * out_rows[r * d .. r * d + d).  The arithmetic is the same attend_row().
  * ------------------------------------------------------------------------- */
-int oracle_attn_rows(const double* q, const double* k, const double* v,
-                     int32_t batch, const int32_t* cu_seqlens_q, const int32_t* past_len,
-                     int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
-                     int32_t window, const double* sink, double scale,
-                     int64_t n_rows, const int64_t* row_tok, const int32_t* row_head,
-                     double* out_rows, int32_t nthreads)
+int oracle_attn_rows_lse(const double* q, const double* k, const double* v,
+                         int32_t batch, const int32_t* cu_seqlens_q, const int32_t* past_len,
+                         int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                         int32_t window, const double* sink, double scale,
+                         int64_t n_rows, const int64_t* row_tok, const int32_t* row_head,
+                         double* out_rows, double* lse_rows, int32_t nthreads)
 {
     int64_t r, tokens;
     int32_t group;
@@ -220,12 +248,25 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
             const double* vh = v + (((int64_t)b * h_kv + g) * s_cap) * d;
             double* score = (double*)malloc(sizeof(double) * (size_t)(skv > 0 ? skv : 1));
             attend_row(q + (tok * h_q + h) * d, kh, vh, d, skv, past_len[b], i, window,
-                       sink ? sink[h] : -INFINITY, scale, score, out_rows + r * d);
+                       sink ? sink[h] : -INFINITY, scale, score, out_rows + r * d,
+                       lse_rows ? lse_rows + r : NULL);
             free(score);
         }
     }
     (void)nthreads;
     return 0;
+}
+
+int oracle_attn_rows(const double* q, const double* k, const double* v,
+                     int32_t batch, const int32_t* cu_seqlens_q, const int32_t* past_len,
+                     int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                     int32_t window, const double* sink, double scale,
+                     int64_t n_rows, const int64_t* row_tok, const int32_t* row_head,
+                     double* out_rows, int32_t nthreads)
+{
+    return oracle_attn_rows_lse(q, k, v, batch, cu_seqlens_q, past_len, h_q, h_kv, d, s_cap,
+                                window, sink, scale, n_rows, row_tok, row_head, out_rows, NULL,
+                                nthreads);
 }
 
 /* ---------------------------------------------------------------------------
