@@ -22,7 +22,8 @@ LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last
 
 _DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
 
-EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_last_error", "attn_tune_stats",
+EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_split",
+            "attn_split_workspace_bytes", "attn_last_error", "attn_tune_stats",
             "attn_tune_reset", "attn_tuned_config", "attn_config_count", "attn_config_name",
             "attn_force_config")
 
@@ -66,6 +67,13 @@ def lib():
                                       ctypes.c_float, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                       ctypes.POINTER(TileLog), _vp]
     L.attn_prefill_varlen.restype = ctypes.c_int
+    L.attn_prefill_split.argtypes = [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp,
+                                     ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _vp, ctypes.c_int64, ctypes.POINTER(TileLog),
+                                     _vp]
+    L.attn_prefill_split.restype = ctypes.c_int
+    L.attn_split_workspace_bytes.argtypes = [ctypes.c_int64, _i32, _i32, _i32]
+    L.attn_split_workspace_bytes.restype = ctypes.c_int64
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_tune_stats.argtypes = [_i64p, _i64p, _i64p]
@@ -160,6 +168,50 @@ def attn_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, past_len, window, hea
     code = lib().attn_prefill_varlen(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
         float(scale), _ptr(out), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype],
+        ctypes.byref(log) if log is not None else None, _stream(stream))
+    if check:
+        _check(code)
+    if log is not None:
+        return code, log.n_records, log.bkv, log.q_rows
+    return code
+
+
+def attn_split_workspace_bytes(q_tokens, h_q, d, n_split):
+    return lib().attn_split_workspace_bytes(int(q_tokens), int(h_q), int(d), int(n_split))
+
+
+def attn_prefill_split(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head_sink, scale,
+                       out, lse=None, n_split=1, workspace=None, tile_log=None, stream=None,
+                       check=True):
+    """attn_prefill_varlen with a log-sum-exp side output (lse: float32 [tokens, h_q] or
+    None) and KV splits across workgroups (workspace: a device tensor of at least
+    attn_split_workspace_bytes(...) bytes when n_split > 1)."""
+    _require(q, "q", 3)
+    _require(out, "out", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    tokens, h_q, d = q.shape
+    batch, h_kv, s_cap, _ = k_cache.shape
+    nseq = len(past_len)
+    if len(cu_seqlens_q) != nseq + 1:
+        raise ValueError("cu_seqlens_q must have len(past_len) + 1 entries")
+    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
+    pl = (ctypes.c_int32 * max(1, nseq))(*[int(x) for x in past_len])
+    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
+        raise ValueError("head_sink must be a contiguous float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (tokens, h_q)):
+        raise ValueError("lse must be a contiguous float32 tensor [tokens, h_q]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    log = None
+    if tile_log is not None:
+        if tile_log.dtype != torch.int32 or tile_log.dim() != 2 or tile_log.shape[1] != 8:
+            raise ValueError("tile_log must be an int32 tensor [capacity, 8]")
+        log = TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
+    code = lib().attn_prefill_split(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
+        float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype],
+        _DTYPE_CODE[out.dtype], int(n_split), _ptr(workspace), int(ws_bytes),
         ctypes.byref(log) if log is not None else None, _stream(stream))
     if check:
         _check(code)

@@ -101,7 +101,20 @@ struct Call {
   float scale;
   attn_tile_log* log;
   hipStream_t stream;
+  // log-sum-exp output and KV splits (attn_prefill_split); defaults: none, 1
+  float* lse = nullptr;
+  int32_t n_split = 1;
+  void* workspace = nullptr;
+  int64_t workspace_bytes = 0;
 };
+
+constexpr int32_t kMaxSplit = 64;
+
+// Workspace of a split call: partial outputs [n_split, tokens, h_q, d] fp32,
+// then partial log-sum-exps [n_split, tokens, h_q] fp32.
+int64_t split_workspace_bytes(int64_t tokens, int64_t h_q, int64_t d, int64_t n_split) {
+  return n_split <= 1 ? 0 : n_split * tokens * h_q * (d + 1) * (int64_t)sizeof(float);
+}
 
 int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
@@ -132,6 +145,15 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
   p.s_cap = c.s_cap;
   p.window = c.window > 0 ? c.window : 0;
   p.scale_log2 = c.scale * 1.4426950408889634f;
+  const int64_t tokens = c.cu[c.batch] - c.cu[0];
+  p.n_split = c.n_split;
+  p.ws_tokens = (int32_t)tokens;
+  if (c.n_split > 1) {
+    p.ws_o = static_cast<float*>(c.workspace);
+    p.ws_lse = p.ws_o + (int64_t)c.n_split * tokens * c.h_q * c.d;
+  } else {
+    p.lse = c.lse;
+  }
 
   int64_t written = 0;
   for (int32_t b0 = 0; b0 < c.batch; b0 += attn::kMaxSeq) {
@@ -154,7 +176,22 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
     p.log = log_base ? log_base + written * ATTN_LOG_FIELDS : nullptr;
     hipError_t e = fn(p, (int)n_items, c.stream);
     if (e != hipSuccess) return fail(ATTN_EHIP, "kernel launch: %s", hipGetErrorString(e));
-    written += n_items;
+    written += n_items * c.n_split;
+  }
+  if (c.n_split > 1) {
+    attn::MergeParams mp;
+    mp.ws_o = p.ws_o;
+    mp.ws_lse = p.ws_lse;
+    mp.sink = with_sink ? c.sink : nullptr;
+    mp.out = c.out;
+    mp.lse = c.lse;
+    mp.tokens = (int32_t)tokens;
+    mp.h_q = c.h_q;
+    mp.d = c.d;
+    mp.n_split = c.n_split;
+    hipError_t e = attn::launch_merge(mp, c.out_dtype == ATTN_F32, c.out_dtype == ATTN_BF16,
+                                      c.stream);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "merge launch: %s", hipGetErrorString(e));
   }
   if (n_records) *n_records = written;
   return ATTN_OK;
@@ -166,7 +203,7 @@ int64_t plan_items(const Call& c, int cfg_index) {
   const int q_rows = attn::config(cfg_index).rows / hpack;
   int64_t tiles = 0;
   for (int32_t b = 0; b < c.batch; ++b) tiles += (c.cu[b + 1] - c.cu[b] + q_rows - 1) / q_rows;
-  return tiles * c.h_kv * (group / hpack);
+  return tiles * c.h_kv * (group / hpack) * c.n_split;
 }
 
 // The key leaves out the KV depth, so its one sweep stands for every depth
@@ -230,7 +267,7 @@ int choose_config(const Call& c, int* cfg) {
   }
   const int64_t tokens = c.cu[c.batch] - c.cu[0];
   TuneKey key{c.d, c.dtype, c.out_dtype, tokens, c.h_q, c.h_q / c.h_kv,
-              c.window > 0 ? c.window : 0, c.batch, 0};
+              c.window > 0 ? c.window : 0, c.batch, c.n_split};
   std::lock_guard<std::mutex> lk(g_tune_mu);
   auto it = g_tune.find(key);
   if (it != g_tune.end()) { *cfg = it->second; return ATTN_OK; }
@@ -269,6 +306,14 @@ int validate(const Call& c) {
     if (c.log->capacity < 0 || (c.log->capacity > 0 && !c.log->records))
       return fail(ATTN_EINVAL, "bad tile log");
   }
+  if (c.n_split < 1 || c.n_split > kMaxSplit)
+    return fail(ATTN_EINVAL, "n_split %d outside 1..%d", c.n_split, kMaxSplit);
+  if (c.n_split > 1 && tokens > 0) {
+    const int64_t need = split_workspace_bytes(tokens, c.h_q, c.d, c.n_split);
+    if (!c.workspace || c.workspace_bytes < need)
+      return fail(ATTN_EINVAL, "split workspace holds %lld bytes, %lld needed",
+                  (long long)c.workspace_bytes, (long long)need);
+  }
   // declines: valid requests this library does not implement
   if (c.d != 64 && c.d != 128) return fail(ATTN_DECLINED, "d=%d not supported (64, 128)", c.d);
   if (c.dtype != ATTN_F16 && c.dtype != ATTN_BF16)
@@ -280,6 +325,8 @@ int validate(const Call& c) {
     auto mis = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; };
     if (mis(c.q) || mis(c.k) || mis(c.v) || mis(c.out))
       return fail(ATTN_DECLINED, "tensor pointers must be 16-byte aligned");
+    if (c.n_split > 1 && mis(c.workspace))
+      return fail(ATTN_DECLINED, "the split workspace must be 16-byte aligned");
   }
   return ATTN_OK;
 }
@@ -355,6 +402,31 @@ int attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
   }
 }
 
+int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
+                       int32_t window, const float* head_sink, float scale, void* out,
+                       float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                       int32_t dtype, int32_t out_dtype, int32_t n_split, void* workspace,
+                       int64_t workspace_bytes, attn_tile_log* tile_log, void* stream) {
+  try {
+    Call c{q, k_cache, v_cache, out, head_sink, cu_seqlens_q, past_len, batch, window, h_q,
+           h_kv, d, s_cap, dtype, out_dtype, scale, tile_log,
+           reinterpret_cast<hipStream_t>(stream)};
+    c.lse = lse;
+    c.n_split = n_split;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    return run(c);
+  } catch (...) {
+    return fail(ATTN_EHIP, "internal error");
+  }
+}
+
+int64_t attn_split_workspace_bytes(int64_t q_tokens, int32_t h_q, int32_t d, int32_t n_split) {
+  if (q_tokens < 0 || h_q <= 0 || d <= 0 || n_split < 1) return -1;
+  return split_workspace_bytes(q_tokens, h_q, d, n_split);
+}
+
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
 int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys) {
@@ -376,7 +448,7 @@ int32_t attn_tuned_config(int32_t d, int32_t dtype, int32_t out_dtype, int64_t q
                           int32_t h_q, int32_t h_kv, int32_t window, int32_t batch) {
   if (h_kv <= 0) return -1;
   const TuneKey key{d, dtype, out_dtype, q_tokens, h_q, h_q / h_kv, window > 0 ? window : 0,
-                    batch, 0};
+                    batch, 1};  // the key of unsplit calls
   std::lock_guard<std::mutex> lk(g_tune_mu);
   auto it = g_tune.find(key);
   return it == g_tune.end() ? -1 : it->second;

@@ -33,8 +33,26 @@ struct Params {
   int32_t s_cap;
   int32_t window;
   float scale_log2;    // scale * log2(e)
+  // Optional outputs and KV splits across workgroups (blockIdx.y):
+  float* lse;          // [tokens, h_q] log-sum-exp of kept scores (natural log, no sink), or nullptr
+  float* ws_o;         // n_split > 1: partial outputs [n_split, ws_tokens, h_q, d] (fp32)
+  float* ws_lse;       // n_split > 1: partial log-sum-exp [n_split, ws_tokens, h_q] (log2 units)
+  int32_t n_split;     // 1: the kernel writes `out`; > 1: it writes partials for attn merge
+  int32_t ws_tokens;   // q rows of the whole call (workspace stride)
   SeqTable seq;
 };
+
+// Combine n_split partial results (and the sink) into out / lse.
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_lse;
+  const float* sink;   // [h_q] or nullptr
+  void* out;
+  float* lse;          // or nullptr
+  int32_t tokens, h_q, d, n_split;
+};
+hipError_t launch_merge(const MergeParams& mp, int out_dtype_is_f32, int out_is_bf16,
+                        hipStream_t stream);
 
 enum DType { kF16 = 1, kBF16 = 2, kF32 = 3 };
 

@@ -64,6 +64,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct F16 {
   static constexpr bool kSplitP = false;
@@ -207,6 +208,72 @@ __device__ inline uint32_t lds_byte_addr(const void* p) {
 constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | (15 << 8) | (7 << 4) | (n & 15); }
 __device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Final epilogue of one row (each lane holds half of the row's output
+// columns).  XTRA: compiled with the log-sum-exp output and the split
+// partials (the plain instantiations carry neither).  m_run: the row's reference max in log2 units of the scaled
+// scores; l_kept: its full sum of P over the kept keys (both lane halves).
+//   n_split == 1: out = acc / (l_kept + exp2(sink - m)), converted to the
+//     output type; with p.lse, the row's log-sum-exp (natural log, sink
+//     excluded) = (m + log2 l_kept) ln 2.
+//   n_split > 1: the workgroup's partial result for the merge kernel:
+//     acc / l_kept in fp32 and m + log2 l_kept (log2 units), or 0 and -inf
+//     when this part of the KV range kept no key of the row.
+template <int D, bool XTRA, typename TI, typename TO>
+__device__ inline void finish_row(const Params& p, const f32x16* acc, float m_run, float l_kept,
+                                  int64_t tok, int head, int half) {
+  constexpr int DB = D / 32;
+  const float kNegInf = -__builtin_inff();
+  const int64_t row = tok * p.h_q + head;
+  const bool any = m_run != kNegInf;
+  if (XTRA && p.n_split > 1) {
+    const int64_t prow = (int64_t)blockIdx.y * p.ws_tokens * p.h_q + row;
+    const float inv = any ? 1.f / l_kept : 0.f;
+    float* o = p.ws_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = db * 32 + i4 * 8 + half * 4;
+        *reinterpret_cast<f32x4*>(o + d0) =
+            f32x4{acc[db][i4 * 4 + 0] * inv, acc[db][i4 * 4 + 1] * inv,
+                  acc[db][i4 * 4 + 2] * inv, acc[db][i4 * 4 + 3] * inv};
+      }
+    if (half == 0) p.ws_lse[prow] = any ? m_run + __builtin_amdgcn_logf(l_kept) : kNegInf;
+    return;
+  }
+  float l_tot = l_kept;
+  if (p.sink != nullptr && any) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
+  const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
+  const int64_t ooff = row * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = db * 32 + i4 * 8 + half * 4;
+      const float o0 = acc[db][i4 * 4 + 0] * inv, o1 = acc[db][i4 * 4 + 1] * inv;
+      const float o2 = acc[db][i4 * 4 + 2] * inv, o3 = acc[db][i4 * 4 + 3] * inv;
+      if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
+            f32x4{o0, o1, o2, o3};
+      } else {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
+            u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
+      }
+    }
+  if (XTRA && p.lse != nullptr && half == 0)
+    p.lse[row] = any ? (m_run + __builtin_amdgcn_logf(l_kept)) * kLn2 : kNegInf;
+}
+
+// This workgroup's part of the Q tile's KV tiles [t_lo, t_hi] when the range
+// is cut into p.n_split contiguous parts (blockIdx.y); may come out empty.
+__device__ inline void split_range(const Params& p, int* t_lo, int* t_hi) {
+  if (p.n_split <= 1) return;
+  const int per = (*t_hi - *t_lo + p.n_split) / p.n_split;  // ceil(tiles / n_split)
+  const int lo = *t_lo + (int)blockIdx.y * per;
+  *t_hi = min(*t_hi, lo + per - 1);
+  *t_lo = lo;
+}
+
 // Workgroup = R row groups x S KV splits of one wave each.  Row group rg owns
 // 32 Q-tile rows; split sp takes every S-th KV tile of the workgroup's range,
 // so the S waves of a row group (two per SIMD) work on different tiles at
@@ -222,7 +289,8 @@ __device__ inline float vmax(float a, float b) { return __builtin_elementwise_ma
 //                                                    tiles), its max, the
 //                                                    rescale test
 // so matrix and vector work of neighbouring tiles overlap inside the wave.
-template <int D, int BKV, int R, int S_REQ, int NSLOT, bool WIN, typename TI, typename TO>
+template <int D, int BKV, int R, int S_REQ, int NSLOT, bool WIN, bool XTRA, typename TI,
+          typename TO>
 __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kernel(Params p) {
   // stages of two 64-key d=128 tiles would not fit in LDS: d=128 uses one split
   constexpr int S = (D == 128) ? 1 : S_REQ;
@@ -278,9 +346,10 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
 
   // KV tiles of the whole Q tile: floor from the first row, ceiling from the last
   const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
-  const int t_lo = lo_key / BKV;
-  const int t_hi = (past + q_last) / BKV;
-  const int n_stages = (t_hi - t_lo + S) / S;
+  int t_lo = lo_key / BKV;
+  int t_hi = (past + q_last) / BKV;
+  if constexpr (XTRA) split_range(p, &t_lo, &t_hi);
+  const int n_stages = max(0, (t_hi - t_lo + S) / S);
 
   // ---- this lane's row ----
   const int row = rg * 32 + col;
@@ -623,35 +692,12 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
 
   // ---- epilogue: combine lane halves, fold the sink, normalise, store ----
   if (sp == 0) {
-    float l_tot = l_run + other_half(l_run);
-    if (p.sink != nullptr && m_run != kNegInf) {
-      const float sk = p.sink[head];
-      l_tot += __builtin_amdgcn_exp2f(sk * kLog2e - m_run);
-    }
-    const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
-
-    if (valid) {
-      const int64_t ooff = ((tok0 + pos) * p.h_q + head) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = db * 32 + i4 * 8 + half * 4;
-          const float o0 = acc[db][i4 * 4 + 0] * inv, o1 = acc[db][i4 * 4 + 1] * inv;
-          const float o2 = acc[db][i4 * 4 + 2] * inv, o3 = acc[db][i4 * 4 + 3] * inv;
-          if constexpr (sizeof(TO) == 4) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
-                f32x4{o0, o1, o2, o3};
-          } else {
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
-                u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
-          }
-        }
-    }
+    const float l_kept = l_run + other_half(l_run);
+    if (valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_kept, tok0 + pos, head, half);
   }
 
   if (p.log != nullptr && tid == 0) {
-    int32_t* rec = p.log + (int64_t)blockIdx.x * 8;
+    int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 8;
     rec[0] = slot;
     rec[1] = g * p.group + hg * p.hpack;
     rec[2] = p.hpack;
@@ -676,7 +722,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
 // one wave's MFMA burst runs beside the other wave's exp2 / VALU burst.
 // Each group owns an NS-slot ring of (K, V) tiles in LDS, filled by its own
 // four waves.
-template <int D, int BKV_REQ, int NS_REQ, bool WIN, typename TI, typename TO>
+template <int D, int BKV_REQ, int NS_REQ, bool WIN, bool XTRA, typename TI, typename TO>
 __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   constexpr int BKV = (D == 128) ? 32 : BKV_REQ;  // ring of 2 x NS tiles must fit LDS
   constexpr int NS = (D == 128) ? 4 : NS_REQ;      // (a 5-deep ring spills at d = 128)
@@ -731,9 +777,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   const int window = WIN ? p.window : 0;
 
   const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
-  const int t_lo = lo_key / BKV;
-  const int t_hi = (past + q_last) / BKV;
-  const int n_stages = (t_hi - t_lo + 2) / 2;  // tiles of group 0 (group 1: same or one fewer)
+  int t_lo = lo_key / BKV;
+  int t_hi = (past + q_last) / BKV;
+  if constexpr (XTRA) split_range(p, &t_lo, &t_hi);
+  const int n_stages = max(0, (t_hi - t_lo + 2) / 2);  // group 0's tiles (group 1: same or one fewer)
 
   const int row = rg * 32 + col;
   const int pos = q0 + row / p.hpack;
@@ -1089,35 +1136,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     }
   }
 
-  if (grp == 0) {
-    float l_tot = l_run;
-    if (p.sink != nullptr && m_run != kNegInf) {
-      const float sk = p.sink[head];
-      l_tot += __builtin_amdgcn_exp2f(sk * kLog2e - m_run);
-    }
-    const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
-    if (valid) {
-      const int64_t ooff = ((tok0 + pos) * p.h_q + head) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = db * 32 + i4 * 8 + half * 4;
-          const float o0 = acc[db][i4 * 4 + 0] * inv, o1 = acc[db][i4 * 4 + 1] * inv;
-          const float o2 = acc[db][i4 * 4 + 2] * inv, o3 = acc[db][i4 * 4 + 3] * inv;
-          if constexpr (sizeof(TO) == 4) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
-                f32x4{o0, o1, o2, o3};
-          } else {
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
-                u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
-          }
-        }
-    }
-  }
+  if (grp == 0 && valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_run, tok0 + pos, head, half);
 
   if (p.log != nullptr && tid == 0) {
-    int32_t* rec = p.log + (int64_t)blockIdx.x * 8;
+    int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 8;
     rec[0] = slot;
     rec[1] = g * p.group + hg * p.hpack;
     rec[2] = p.hpack;
@@ -1129,27 +1151,43 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   }
 }
 
+template <int D, int BKV, int NS, bool XTRA, typename TI, typename TO>
+void launch_pp_x(const Params& p, int n_items, hipStream_t stream) {
+  if (p.window > 0)
+    hipLaunchKernelGGL((attn_pp_kernel<D, BKV, NS, true, XTRA, TI, TO>),
+                       dim3(n_items, p.n_split), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_pp_kernel<D, BKV, NS, false, XTRA, TI, TO>),
+                       dim3(n_items, p.n_split), dim3(512), 0, stream, p);
+}
+
 template <int D, int BKV, int NS, typename TI, typename TO>
 hipError_t launch_pp(const Params& p, int n_items, hipStream_t stream) {
-  if (p.window > 0)
-    hipLaunchKernelGGL((attn_pp_kernel<D, BKV, NS, true, TI, TO>), dim3(n_items), dim3(512), 0,
-                       stream, p);
+  if (p.n_split > 1 || p.lse != nullptr)
+    launch_pp_x<D, BKV, NS, true, TI, TO>(p, n_items, stream);
   else
-    hipLaunchKernelGGL((attn_pp_kernel<D, BKV, NS, false, TI, TO>), dim3(n_items), dim3(512), 0,
-                       stream, p);
+    launch_pp_x<D, BKV, NS, false, TI, TO>(p, n_items, stream);
   return hipGetLastError();
 }
 
 
-template <int D, int BKV, int R, int S, int NS, typename TI, typename TO>
-hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
+template <int D, int BKV, int R, int S, int NS, bool XTRA, typename TI, typename TO>
+void launch_x(const Params& p, int n_items, hipStream_t stream) {
   constexpr int threads = R * (D == 128 ? 1 : S) * 64;
   if (p.window > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, true, TI, TO>), dim3(n_items),
-                       dim3(threads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, true, XTRA, TI, TO>),
+                       dim3(n_items, p.n_split), dim3(threads), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, false, TI, TO>), dim3(n_items),
-                       dim3(threads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, false, XTRA, TI, TO>),
+                       dim3(n_items, p.n_split), dim3(threads), 0, stream, p);
+}
+
+template <int D, int BKV, int R, int S, int NS, typename TI, typename TO>
+hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
+  if (p.n_split > 1 || p.lse != nullptr)
+    launch_x<D, BKV, R, S, NS, true, TI, TO>(p, n_items, stream);
+  else
+    launch_x<D, BKV, R, S, NS, false, TI, TO>(p, n_items, stream);
   return hipGetLastError();
 }
 
@@ -1161,6 +1199,62 @@ constexpr KernelConfig make_config(const char* name) {
         {launch<64, BKV, R, S, NS, BF16, uint16_t>, launch<64, BKV, R, S, NS, BF16, float>}},
        {{launch<128, BKV, R, S, NS, F16, uint16_t>, launch<128, BKV, R, S, NS, F16, float>},
         {launch<128, BKV, R, S, NS, BF16, uint16_t>, launch<128, BKV, R, S, NS, BF16, float>}}}};
+}
+
+// ---------------------------------------------------------------------------
+// Merge of KV-split partial results (one thread per 4 output columns of a
+// row).  With lse_s the partials' log2 log-sum-exp and M their maximum:
+// out = sum_s 2^(lse_s - M) o_s / (sum_s 2^(lse_s - M) + 2^(sink log2 e - M)),
+// lse = (M + log2 sum_s 2^(lse_s - M)) ln 2; a row no part kept gives 0, -inf.
+template <int D, int OUT>  // OUT: 0 fp16, 1 bf16, 2 fp32
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
+  constexpr int TPR = D / 4;
+  const int64_t rows = (int64_t)mp.tokens * mp.h_q;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (row >= rows) return;
+  const int c = (threadIdx.x % TPR) * 4;
+  const int head = (int)(row % mp.h_q);
+  const float kNegInf = -__builtin_inff();
+  float mx = kNegInf;
+  for (int s = 0; s < mp.n_split; ++s) mx = fmaxf(mx, mp.ws_lse[s * rows + row]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < mp.n_split; ++s) {
+      const float w = __builtin_amdgcn_exp2f(mp.ws_lse[s * rows + row] - mx);
+      den += w;
+      o += w * *reinterpret_cast<const f32x4*>(mp.ws_o + (s * rows + row) * D + c);
+    }
+  }
+  float tot = den;
+  if (mp.sink != nullptr && mx != kNegInf)
+    tot += __builtin_amdgcn_exp2f(mp.sink[head] * kLog2e - mx);
+  const float inv = mx != kNegInf ? 1.f / tot : 0.f;
+  o *= inv;
+  if constexpr (OUT == 2) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(mp.out) + row * D + c) = o;
+  } else if constexpr (OUT == 1) {
+    bf16x2 a = {(__bf16)o[0], (__bf16)o[1]}, b = {(__bf16)o[2], (__bf16)o[3]};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(mp.out) + row * D + c) =
+        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  } else {
+    f16x2 a = {(_Float16)o[0], (_Float16)o[1]}, b = {(_Float16)o[2], (_Float16)o[3]};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(mp.out) + row * D + c) =
+        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  }
+  if (mp.lse != nullptr && c == 0)
+    mp.lse[row] = mx != kNegInf ? (mx + __builtin_amdgcn_logf(den)) * kLn2 : kNegInf;
+}
+
+template <int D, int OUT>
+hipError_t launch_merge_t(const MergeParams& mp, hipStream_t stream) {
+  constexpr int rows_per_block = 256 / (D / 4);
+  const int64_t rows = (int64_t)mp.tokens * mp.h_q;
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_merge_kernel<D, OUT>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     mp);
+  return hipGetLastError();
 }
 
 // Ping-pong configuration for d = 64; at d = 128 (where its register budget
@@ -1185,6 +1279,18 @@ const KernelConfig kConfigs[] = {
 };
 
 }  // namespace
+
+hipError_t launch_merge(const MergeParams& mp, int out_is_f32, int out_is_bf16,
+                        hipStream_t stream) {
+  const int out = out_is_f32 ? 2 : (out_is_bf16 ? 1 : 0);
+  if (mp.d == 64)
+    return out == 2 ? launch_merge_t<64, 2>(mp, stream)
+                    : (out == 1 ? launch_merge_t<64, 1>(mp, stream)
+                                : launch_merge_t<64, 0>(mp, stream));
+  return out == 2 ? launch_merge_t<128, 2>(mp, stream)
+                  : (out == 1 ? launch_merge_t<128, 1>(mp, stream)
+                              : launch_merge_t<128, 0>(mp, stream));
+}
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
 const KernelConfig& config(int i) { return kConfigs[i]; }

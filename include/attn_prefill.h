@@ -129,6 +129,43 @@ int attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
                         int32_t dtype, int32_t out_dtype,
                         attn_tile_log* tile_log, void* stream);
 
+/*
+ * Ragged batch with a log-sum-exp side output and KV splits across
+ * workgroups (sglang pull request 34468 names the per-row "lse_extend" output
+ * that partial results over disjoint key ranges are merged with; cutting a Q
+ * tile's KV range over several workgroups raises the number of workgroups
+ * when a call has few Q tiles, e.g. one 512-row chunk at a tensor-parallel
+ * rank's 16 q / 2 KV heads).
+ *   arguments as attn_prefill_varlen, plus:
+ *   lse          NULL, or DEVICE float [tokens, h_q]: per row the natural-log
+ *                log-sum-exp of its kept scaled scores, log(sum_k exp(s_k)),
+ *                sink EXCLUDED; -inf for a row that keeps no key.  With
+ *                head_sink = NULL, (out, lse) is the standard pair that
+ *                partial attentions over disjoint key sets merge by.
+ *   n_split      1..64.  1: one workgroup per Q tile walks the whole KV range
+ *                (workspace unused).  > 1: the KV tiles of every Q tile are
+ *                cut into n_split contiguous parts (some may be empty), each
+ *                run by its own workgroup; a second kernel merges the parts,
+ *                folds in the sink and writes out (and lse).
+ *   workspace    DEVICE buffer, 16-byte aligned, of at least
+ *                attn_split_workspace_bytes(tokens, h_q, d, n_split) bytes when
+ *                n_split > 1 (caller-owned; the call overwrites it; calls that
+ *                share one workspace must be ordered on one stream).
+ *   tile_log     records per (work item, split): the split's own tile range.
+ * Errors as attn_prefill_varlen; -2 also for n_split outside 1..64 or a
+ * missing / too small workspace, -1 for a misaligned workspace.
+ */
+int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
+                       int32_t window, const float* head_sink, float scale, void* out,
+                       float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
+                       int32_t dtype, int32_t out_dtype, int32_t n_split, void* workspace,
+                       int64_t workspace_bytes, attn_tile_log* tile_log, void* stream);
+
+/* Bytes of workspace attn_prefill_split needs (0 for n_split = 1; -1 for
+ * invalid sizes): n_split * q_tokens * h_q * (d + 1) * 4. */
+int64_t attn_split_workspace_bytes(int64_t q_tokens, int32_t h_q, int32_t d, int32_t n_split);
+
 /* Text describing the last non-zero return on the calling thread ("" if none). */
 const char* attn_last_error(void);
 
@@ -147,8 +184,9 @@ const char* attn_last_error(void);
  */
 int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys);
 void attn_tune_reset(void);
-/* The configuration index the tuning cache holds for a key (the arguments of
- * a call: q_tokens = rows of q), or -1 if that key has not been swept. */
+/* The configuration index the tuning cache holds for the key of an unsplit
+ * call (its arguments; q_tokens = rows of q), or -1 if that key has not been
+ * swept.  Split calls (attn_prefill_split, n_split > 1) have keys of their own. */
 int32_t attn_tuned_config(int32_t d, int32_t dtype, int32_t out_dtype, int64_t q_tokens,
                           int32_t h_q, int32_t h_kv, int32_t window, int32_t batch);
 

@@ -115,3 +115,26 @@ def test_binding_refuses_bad_tensors():
         binding.attn_prefill(q.transpose(0, 1), k, k, 0, -1, None, 0.1, q)
     with pytest.raises(ValueError):
         binding.attn_prefill(q[0], k, k, 0, -1, None, 0.1, q)
+
+
+def test_split_entry_validates_before_any_gpu_call():
+    L = binding.lib()
+    cu = (ctypes.c_int32 * 2)(0, 64)
+    past = (ctypes.c_int32 * 1)(0)
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+    def call(n_split, ws, ws_bytes):
+        return L.attn_prefill_split(fake, fake, fake, cu, past, 1, -1, None, ctypes.c_float(0.125),
+                                    fake, None, 8, 2, 64, 64, binding.ATTN_F16, binding.ATTN_F16,
+                                    n_split, ws, ws_bytes, None, None)
+
+    need = binding.attn_split_workspace_bytes(64, 8, 64, 4)
+    assert need == 4 * 64 * 8 * 65 * 4
+    assert binding.attn_split_workspace_bytes(64, 8, 64, 1) == 0
+    assert binding.attn_split_workspace_bytes(-1, 8, 64, 2) == -1
+    assert call(0, fake, need) == binding.ATTN_EINVAL
+    assert call(65, fake, need) == binding.ATTN_EINVAL
+    assert call(4, None, need) == binding.ATTN_EINVAL
+    assert call(4, fake, need - 4) == binding.ATTN_EINVAL
+    assert "workspace" in binding.attn_last_error()
+    assert call(4, ctypes.c_void_p(0x10004), need) == binding.ATTN_DECLINED

@@ -1,0 +1,155 @@
+"""GPU parity of the log-sum-exp side output and of KV splits across
+workgroups (attn_prefill_split), against the oracle on the same seeded inputs.
+
+The lse bound: the GPU forms scores in fp32 from fp16 q pre-scaled by
+scale * log2 e (one extra fp16 rounding of q, relative 2^-11) or from exact
+bf16 products; over d <= 128 terms of N(0, 1) inputs that moves a score by
+well under 1e-3, and the lse by no more than the largest score error.  The
+merge adds a few fp32 roundings.  Bound used: |lse_gpu - lse_oracle| <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gqa_flash_attention_prefill_amd import binding, synth
+from parity_helpers import TOL, f64, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 2e-3
+
+CASES = [
+    synth.Case("s_mid_nowin", h_q=8, h_kv=2, d=64, sq=[333], past=[700], window=-1, seed=41),
+    synth.Case("s_mid_w100", h_q=8, h_kv=2, d=64, sq=[300], past=[512], window=100, seed=42),
+    synth.Case("s_tp4", h_q=16, h_kv=2, d=64, sq=[256], past=[1800], window=-1, seed=43),
+    synth.Case("s_bf16_d128", h_q=16, h_kv=2, d=128, sq=[200], past=[450], window=128,
+               dtype="bf16", seed=44),
+    synth.Case("s_ragged", h_q=8, h_kv=2, d=64, sq=[70, 0, 129], past=[0, 40, 900], window=-1,
+               seed=45),
+]
+
+
+def _oracle(inp):
+    sink = None if inp["sink"] is None else f64(inp["sink"])
+    return oracle.attn_prefill_varlen(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]),
+                                      inp["cu_seqlens"], inp["past_len"], inp["window"], sink,
+                                      inp["scale"], return_lse=True)
+
+
+def _run(dev, n_split, out_dtype=torch.float32, log_capacity=0):
+    q = dev["q"]
+    tokens, h_q, d = q.shape
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=q.device)
+    lse = torch.full((tokens, h_q), float("nan"), dtype=torch.float32, device=q.device)
+    nbytes = binding.attn_split_workspace_bytes(tokens, h_q, d, n_split)
+    ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32, device=q.device)
+    log = None
+    if log_capacity:
+        log = torch.full((log_capacity, 8), -7, dtype=torch.int32, device=q.device)
+    res = binding.attn_prefill_split(q, dev["k_cache"], dev["v_cache"], dev["cu_seqlens"],
+                                     dev["past_len"], dev["window"], dev["sink"], dev["scale"],
+                                     out, lse=lse, n_split=n_split, workspace=ws, tile_log=log)
+    torch.cuda.synchronize()
+    if log is None:
+        return out, lse, None
+    _, n, bkv, q_rows = res
+    return out, lse, (log[:n].cpu().numpy(), bkv, q_rows)
+
+
+def _each_config():
+    try:
+        for cfg in range(binding.attn_config_count()):
+            binding.attn_force_config(cfg)
+            yield cfg
+    finally:
+        binding.attn_force_config(-1)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("n_split", [1, 2, 3, 7])
+def test_split_and_lse_match_oracle(case, n_split):
+    inp = synth.make(case)
+    dev = to_device(inp)
+    ref, ref_lse = _oracle(inp)
+    for cfg in _each_config():
+        out, lse, _ = _run(dev, n_split)
+        name = binding.attn_config_name(cfg)
+        assert rel_l2(f64(out), ref) <= TOL, (name, rel_l2(f64(out), ref))
+        err = np.abs(f64(lse) - ref_lse)
+        assert np.all(np.isfinite(f64(lse))), name
+        assert err.max() <= LSE_TOL, (name, float(err.max()))
+
+
+def test_single_split_output_equals_varlen_bitwise():
+    inp = synth.make(CASES[1])
+    dev = to_device(inp)
+    for cfg in _each_config():
+        a, _, _ = _run(dev, 1, out_dtype=torch.float16)
+        b = torch.full_like(a, float("nan"))
+        binding.attn_prefill_varlen(dev["q"], dev["k_cache"], dev["v_cache"], dev["cu_seqlens"],
+                                    dev["past_len"], dev["window"], dev["sink"], dev["scale"], b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), binding.attn_config_name(cfg)
+
+
+def test_more_splits_than_tiles_and_dtype_outputs():
+    # 40 keys per row at most: one or two tiles, so most of the 16 parts are empty
+    case = synth.Case("s_tiny", h_q=4, h_kv=1, d=64, sq=[40], past=[0], window=-1, seed=46)
+    inp = synth.make(case)
+    dev = to_device(inp)
+    ref, ref_lse = _oracle(inp)
+    for out_dtype in (torch.float16, torch.float32):
+        out, lse, _ = _run(dev, 16, out_dtype=out_dtype)
+        assert rel_l2(f64(out), ref) <= TOL
+        assert np.abs(f64(lse) - ref_lse).max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("n_split", [1, 3])
+def test_split_tile_log_partitions_the_tile_range(n_split):
+    case = CASES[4]
+    inp = synth.make(case)
+    dev = to_device(inp)
+    tokens, h_q = inp["q"].shape[0], case.h_q
+    for cfg in _each_config():
+        _, _, (recs, bkv, q_rows) = _run(dev, n_split, log_capacity=4096)
+        cu, past = inp["cu_seqlens"], inp["past_len"]
+        parts = {}
+        for rec in recs:
+            b, h0, nh, q0, q1, tf, tl, n = (int(x) for x in rec)
+            parts.setdefault((b, h0, q0, q1), []).append((tf, tl, n))
+        cover = np.zeros((tokens, h_q), dtype=np.int64)
+        for (b, h0, q0, q1), ps in parts.items():
+            assert len(ps) == n_split
+            lo, hi = oracle.tile_range(past[b], q0, q1, inp["window"], bkv)
+            seen = []
+            for tf, tl, n in ps:
+                if n == 0:
+                    continue
+                assert n == tl - tf + 1
+                seen += list(range(tf, tl + 1))
+            assert sorted(seen) == list(range(lo, hi + 1)), (b, q0, ps, lo, hi)
+        for (b, h0, q0, q1), ps in parts.items():
+            nh = int(recs[0][2])
+            cover[cu[b] + q0:cu[b] + q1 + 1, h0:h0 + nh] += 1
+        assert np.all(cover == 1)
+
+
+def test_tp4_rank_long_prefix_sampled_rows():
+    # one 512-row chunk at gpt-oss-120b TP4 per-rank heads (16 q / 2 KV), 16k
+    # prefix: 64 Q-tile workgroups without splits, 256 with four
+    case = synth.Case("s_tp4_16k", h_q=16, h_kv=2, d=64, sq=[512], past=[15872], window=-1,
+                      seed=47, poison_tail=False)
+    inp = synth.make(case)
+    dev = to_device(inp)
+    out, lse, _ = _run(dev, 4, out_dtype=torch.float16)
+    rng = np.random.default_rng(5)
+    toks = rng.integers(0, 512, size=48)
+    heads = rng.integers(0, 16, size=48).astype(np.int32)
+    sink = f64(inp["sink"])
+    ref, ref_lse = oracle.attn_rows(f64(inp["q"]), f64(inp["k_cache"]), f64(inp["v_cache"]),
+                                    inp["cu_seqlens"], inp["past_len"], -1, sink, inp["scale"],
+                                    toks, heads, return_lse=True)
+    got = f64(out)[toks, heads]
+    assert rel_l2(got, ref) <= TOL
+    assert np.abs(f64(lse)[toks, heads] - ref_lse).max() <= LSE_TOL
