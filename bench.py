@@ -229,12 +229,55 @@ def summarize_counters(fetch_dir, write_dir):
     return res
 
 
+def split_demo(torch, binding):
+    """KV splits across workgroups on calls with few Q tiles: one 512-row chunk
+    after a 15872-key prefix at a tensor-parallel rank's heads (16 q / 2 KV,
+    full attention, sinks), d 64 fp16 and d 128 bf16.  Without splits such a
+    call has 64 Q-tile workgroups for 256 CUs.  Median of 20 calls per point
+    (HIP events on the launch stream); the tuning sweep runs before timing."""
+    import numpy as np
+    from gqa_flash_attention_prefill_amd import synth
+    res = []
+    for d, dtype in ((64, "f16"), (128, "bf16")):
+        case = synth.Case(f"tp4_d{d}", h_q=16, h_kv=2, d=d, sq=[512], past=[15872], window=-1,
+                          dtype=dtype, seed=77, poison_tail=False)
+        inp = synth.make(case, device="cuda")
+        out = torch.empty_like(inp["q"])
+        fl = useful_flops(15872, 512, -1) * 16 / H_Q * d / D
+        row = {"d": d, "dtype": dtype}
+        for n in (1, 2, 4, 8):
+            nbytes = binding.attn_split_workspace_bytes(512, 16, d, n)
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+            def call():
+                binding.attn_prefill_split(inp["q"], inp["k_cache"], inp["v_cache"], [0, 512],
+                                           [15872], -1, inp["sink"], case.scale, out,
+                                           n_split=n, workspace=ws)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(20)]
+            for a, b in ev:
+                a.record()
+                call()
+                b.record()
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+            row[f"n_split_{n}"] = {"us": round(us, 2), "tflops": round(fl / us / 1e6, 1)}
+        res.append(row)
+    return {"workload": "one 512-row chunk, 15872-key prefix, 16 q / 2 KV heads (TP4 rank), "
+                        "full attention, sinks", "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-demo", action="store_true",
+                    help="time KV splits on a few-Q-tile call (prints its own JSON line)")
     ap.add_argument("--detail", default=None, help="write per-chunk timings (JSON) here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run the 1 GiB cold copy used to scale HBM counters")
@@ -258,6 +301,10 @@ def main():
     import torch
     from gqa_flash_attention_prefill_amd import binding
     L = binding.lib()
+    if args.split_demo:
+        torch.cuda.set_device(0)
+        print(json.dumps(split_demo(torch, binding)), flush=True)
+        return
     dev = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
