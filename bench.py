@@ -270,12 +270,57 @@ def split_demo(torch, binding):
                         "full attention, sinks", "results": res}
 
 
+def decode_demo(torch, binding):
+    """One decode step (one query row per sequence) of a 64-sequence batch,
+    every sequence after a 16383-key prefix, H_q 64 / H_kv 8, d 64, fp16,
+    sinks: window 128 and full attention (also with KV splits).  HBM-bound:
+    GB/s of algorithmic bytes (q + out + each sequence's kept K/V keys once)
+    against 8 TB/s.  Median of 20 calls (HIP events on the launch stream)."""
+    import numpy as np
+    from gqa_flash_attention_prefill_amd import synth
+    B, past = 64, 16383
+    case = synth.Case("decode64", h_q=H_Q, h_kv=H_KV, d=D, sq=[1] * B, past=[past] * B,
+                      window=-1, seed=78, poison_tail=False)
+    inp = synth.make(case, device="cuda")
+    out = torch.empty_like(inp["q"])
+    cu = list(range(B + 1))
+    res = {}
+    for label, window, n_split in (("window128", WINDOW, 1), ("full", -1, 1),
+                                   ("full_split2", -1, 2), ("full_split4", -1, 4)):
+        nbytes = binding.attn_split_workspace_bytes(B, H_Q, D, n_split)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        keys = past + 1 if window <= 0 else min(window, past + 1)
+        algo = 2 * (2 * B * H_Q * D + 2 * B * keys * H_KV * D)
+
+        def call():
+            binding.attn_prefill_split(inp["q"], inp["k_cache"], inp["v_cache"], cu, [past] * B,
+                                       window, inp["sink"], case.scale, out, n_split=n_split,
+                                       workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(20)]
+        for a, b in ev:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        res[label] = {"us": round(us, 2), "hbm_gbs": round(algo / us / 1e3, 1),
+                      "frac_of_8tbs": round(algo / us / 1e3 / 8000.0, 4)}
+    return {"workload": "decode step: 64 sequences x 1 row after 16383 cached keys, H_q 64 / "
+                        "H_kv 8, d 64, fp16, sinks", "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-demo", action="store_true",
+                    help="time a 64-sequence decode step (prints its own JSON line)")
     ap.add_argument("--split-demo", action="store_true",
                     help="time KV splits on a few-Q-tile call (prints its own JSON line)")
     ap.add_argument("--detail", default=None, help="write per-chunk timings (JSON) here")
@@ -301,9 +346,10 @@ def main():
     import torch
     from gqa_flash_attention_prefill_amd import binding
     L = binding.lib()
-    if args.split_demo:
+    if args.split_demo or args.decode_demo:
         torch.cuda.set_device(0)
-        print(json.dumps(split_demo(torch, binding)), flush=True)
+        demo = split_demo if args.split_demo else decode_demo
+        print(json.dumps(demo(torch, binding)), flush=True)
         return
     dev = "cuda:0"
     torch.cuda.set_device(0)

@@ -193,6 +193,13 @@ __device__ inline float pair_max(float x) {
 // kernel waits for them with explicit s_waitcnt vmcnt before that barrier).
 __device__ inline void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  // the base is wave-uniform by construction; readfirstlane makes that
+  // visible where the compiler cannot prove it, so it lands in SGPRs
+  // (the builtin returns int: widen through uint32_t, never sign-extend)
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  sbase = reinterpret_cast<const void*>((hi << 32) | lo);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds_addr), "v"(voff), "s"(sbase)
@@ -1276,6 +1283,10 @@ const KernelConfig kConfigs[] = {
     make_config<64, 4, 2>("r128_kv64_s2"),
     make_config<64, 4, 1>("r128_kv64_s1"),
     make_config<32, 2, 2>("r64_kv32_s2"),
+    // 32-row Q tiles (one row group, two KV-split waves, 48 KB of LDS) for
+    // calls with few rows per sequence, e.g. decode steps (one position x the
+    // KV group's heads)
+    make_config<32, 1, 2>("r32_kv32_s2"),
 };
 
 }  // namespace
