@@ -229,12 +229,45 @@ def summarize_counters(fetch_dir, write_dir):
     return res
 
 
+def _time_calls(torch, binding, args, reps=20):
+    """Mean us per call of `reps` back-to-back attn_prefill_split calls with
+    pre-marshalled arguments, between one event pair on the launch stream
+    (per-call events would add their own queue work to calls this short)."""
+    L = binding.lib()
+    for _ in range(3):
+        rc = L.attn_prefill_split(*args)
+        if rc != 0:
+            raise RuntimeError(binding.attn_last_error())
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        L.attn_prefill_split(*args)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def _split_args(torch, binding, inp, case, cu, past, window, out, n_split, ws):
+    import ctypes
+    cu_a = (ctypes.c_int32 * len(cu))(*cu)
+    past_a = (ctypes.c_int32 * len(past))(*past)
+    code = {torch.float16: binding.ATTN_F16, torch.bfloat16: binding.ATTN_BF16}
+    batch, h_kv, s_cap, d = inp["k_cache"].shape
+    return (ctypes.c_void_p(inp["q"].data_ptr()), ctypes.c_void_p(inp["k_cache"].data_ptr()),
+            ctypes.c_void_p(inp["v_cache"].data_ptr()), cu_a, past_a, len(past), window,
+            ctypes.c_void_p(inp["sink"].data_ptr()), ctypes.c_float(case.scale),
+            ctypes.c_void_p(out.data_ptr()), None, inp["q"].shape[1], h_kv, d, s_cap,
+            code[inp["q"].dtype], code[out.dtype], n_split, ctypes.c_void_p(ws.data_ptr()),
+            ws.numel(), None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
 def split_demo(torch, binding):
     """KV splits across workgroups on calls with few Q tiles: one 512-row chunk
     after a 15872-key prefix at a tensor-parallel rank's heads (16 q / 2 KV,
     full attention, sinks), d 64 fp16 and d 128 bf16.  Without splits such a
-    call has 64 Q-tile workgroups for 256 CUs.  Median of 20 calls per point
-    (HIP events on the launch stream); the tuning sweep runs before timing."""
+    call has 64 Q-tile workgroups for 256 CUs.  Mean of 20 back-to-back calls
+    per point (see _time_calls); the tuning sweep runs before timing."""
     import numpy as np
     from gqa_flash_attention_prefill_amd import synth
     res = []
@@ -248,22 +281,8 @@ def split_demo(torch, binding):
         for n in (1, 2, 4, 8):
             nbytes = binding.attn_split_workspace_bytes(512, 16, d, n)
             ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
-
-            def call():
-                binding.attn_prefill_split(inp["q"], inp["k_cache"], inp["v_cache"], [0, 512],
-                                           [15872], -1, inp["sink"], case.scale, out,
-                                           n_split=n, workspace=ws)
-            for _ in range(3):
-                call()
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(20)]
-            for a, b in ev:
-                a.record()
-                call()
-                b.record()
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+            args = _split_args(torch, binding, inp, case, [0, 512], [15872], -1, out, n, ws)
+            us = _time_calls(torch, binding, args)
             row[f"n_split_{n}"] = {"us": round(us, 2), "tflops": round(fl / us / 1e6, 1)}
         res.append(row)
     return {"workload": "one 512-row chunk, 15872-key prefix, 16 q / 2 KV heads (TP4 rank), "
@@ -275,7 +294,7 @@ def decode_demo(torch, binding):
     every sequence after a 16383-key prefix, H_q 64 / H_kv 8, d 64, fp16,
     sinks: window 128 and full attention (also with KV splits).  HBM-bound:
     GB/s of algorithmic bytes (q + out + each sequence's kept K/V keys once)
-    against 8 TB/s.  Median of 20 calls (HIP events on the launch stream)."""
+    against 8 TB/s.  Mean of 20 back-to-back calls (see _time_calls)."""
     import numpy as np
     from gqa_flash_attention_prefill_amd import synth
     B, past = 64, 16383
@@ -291,22 +310,8 @@ def decode_demo(torch, binding):
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
         keys = past + 1 if window <= 0 else min(window, past + 1)
         algo = 2 * (2 * B * H_Q * D + 2 * B * keys * H_KV * D)
-
-        def call():
-            binding.attn_prefill_split(inp["q"], inp["k_cache"], inp["v_cache"], cu, [past] * B,
-                                       window, inp["sink"], case.scale, out, n_split=n_split,
-                                       workspace=ws)
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(20)]
-        for a, b in ev:
-            a.record()
-            call()
-            b.record()
-        torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        args = _split_args(torch, binding, inp, case, cu, [past] * B, window, out, n_split, ws)
+        us = _time_calls(torch, binding, args)
         res[label] = {"us": round(us, 2), "hbm_gbs": round(algo / us / 1e3, 1),
                       "frac_of_8tbs": round(algo / us / 1e3 / 8000.0, 4)}
     return {"workload": "decode step: 64 sequences x 1 row after 16383 cached keys, H_q 64 / "
