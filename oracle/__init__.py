@@ -46,6 +46,10 @@ def _load():
         _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _dp,
         ctypes.c_double, _dp, _dp, _i32]
     lib.oracle_attn_prefill_varlen_lse.restype = ctypes.c_int
+    lib.oracle_attn_prefill_varlen_ex.argtypes = [
+        _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _i32, _dp,
+        ctypes.c_double, _dp, _dp, _i32]
+    lib.oracle_attn_prefill_varlen_ex.restype = ctypes.c_int
     lib.oracle_attn_rows.argtypes = [
         _dp, _dp, _dp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32, _dp,
         ctypes.c_double, _i64, _i64p, _i32p, _dp, _i32]
@@ -80,9 +84,10 @@ def _i32arr(a):
 
 
 def attn_prefill_varlen(q, k, v, cu_seqlens_q, past_len, window, sink, scale, threads=0,
-                        return_lse=False):
+                        return_lse=False, causal=True):
     """Full output [tokens, h_q, d] in float64 (see attn_oracle.c); with
-    return_lse, also the log-sum-exp [tokens, h_q] of each row's kept scores."""
+    return_lse, also the log-sum-exp [tokens, h_q] of each row's kept scores;
+    causal=False keeps every key of the sequence (above the window's floor)."""
     lib = _load()
     q, qp = _f64(q)
     k, kp = _f64(k)
@@ -99,11 +104,11 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, past_len, window, sink, scale, th
         sp = None
     out = np.zeros((tokens, h_q, d), dtype=np.float64)
     lse = np.zeros((tokens, h_q), dtype=np.float64) if return_lse else None
-    rc = lib.oracle_attn_prefill_varlen_lse(qp, kp, vp, batch, cup, plp, h_q, h_kv, d, s_cap,
-                                            int(window), sp, float(scale),
-                                            out.ctypes.data_as(_dp),
-                                            lse.ctypes.data_as(_dp) if return_lse else None,
-                                            int(threads))
+    rc = lib.oracle_attn_prefill_varlen_ex(qp, kp, vp, batch, cup, plp, h_q, h_kv, d, s_cap,
+                                           int(window), 1 if causal else 0, sp, float(scale),
+                                           out.ctypes.data_as(_dp),
+                                           lse.ctypes.data_as(_dp) if return_lse else None,
+                                           int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attn_prefill_varlen rejected its arguments ({rc})")
     return (out, lse) if return_lse else out

@@ -58,18 +58,32 @@
  * itself and window = 1 keeps only the diagonal key ("harness: window
  * cases").  window <= 0 disables the lower bound.
  * ------------------------------------------------------------------------- */
-static int kept(int64_t past_len, int64_t q, int64_t k, int64_t window)
+static int kept_ex(int64_t past_len, int64_t q, int64_t k, int64_t window, int causal)
 {
     int64_t pos = past_len + q;
-    if (k < 0 || k > pos) return 0;
+    if (k < 0) return 0;
+    if (causal && k > pos) return 0;
     if (window > 0 && k < pos - window + 1) return 0;
     return 1;
+}
+
+static int kept(int64_t past_len, int64_t q, int64_t k, int64_t window)
+{
+    return kept_ex(past_len, q, k, window, 1);
 }
 
 int oracle_kept(int64_t past_len, int64_t q, int64_t k, int64_t window)
 {
     return kept(past_len, q, k, window);
 }
+
+/* Non-causal attention (sglang pull request 34468 tests its kernel "causal
+ * and non-causal"): the row no longer stops at its own position; it keeps
+ * every key of its sequence, k < past_len + sq, still above the window's
+ * lower bound when a window is given (reading: the window's lower bound is
+ * a mask of its own, independent of causality, as in the page's kernel,
+ * whose window mask keeps q <= kv + SLIDING_WINDOW_SIZE alongside the
+ * optional causal mask).  The key range k < skv is the caller's loop bound. */
 
 /* ---------------------------------------------------------------------------
  * One output row.  Softmax over the kept scores and the sink logit, with
@@ -86,7 +100,8 @@ int oracle_kept(int64_t past_len, int64_t q, int64_t k, int64_t window)
  * ------------------------------------------------------------------------- */
 static void attend_row(const double* q_row, const double* k_head, const double* v_head,
                        int64_t d, int64_t skv, int64_t past_len, int64_t q, int64_t window,
-                       double sink, double scale, double* score, double* out, double* lse)
+                       int causal, double sink, double scale, double* score, double* out,
+                       double* lse)
 {
     int64_t j, t;
     int any = 0;
@@ -94,7 +109,7 @@ static void attend_row(const double* q_row, const double* k_head, const double* 
 
     /* 1. the full score row S[j] = scale * <q, k_j>, masked entries -inf */
     for (j = 0; j < skv; ++j) {
-        if (!kept(past_len, q, j, window)) { score[j] = -INFINITY; continue; }
+        if (!kept_ex(past_len, q, j, window, causal)) { score[j] = -INFINITY; continue; }
         double dot = 0.0;
         for (t = 0; t < d; ++t) dot += q_row[t] * k_head[j * d + t];
         score[j] = scale * dot;
@@ -162,11 +177,12 @@ static int check_batch(int32_t batch, const int32_t* cu_seqlens_q, const int32_t
  *   nthreads     : OpenMP threads (<= 0: the runtime default)
  * Returns 0, or -2 on an invalid argument.
  * ------------------------------------------------------------------------- */
-int oracle_attn_prefill_varlen_lse(const double* q, const double* k, const double* v,
-                                   int32_t batch, const int32_t* cu_seqlens_q,
-                                   const int32_t* past_len, int32_t h_q, int32_t h_kv, int32_t d,
-                                   int32_t s_cap, int32_t window, const double* sink,
-                                   double scale, double* out, double* lse, int32_t nthreads)
+int oracle_attn_prefill_varlen_ex(const double* q, const double* k, const double* v,
+                                  int32_t batch, const int32_t* cu_seqlens_q,
+                                  const int32_t* past_len, int32_t h_q, int32_t h_kv, int32_t d,
+                                  int32_t s_cap, int32_t window, int32_t causal,
+                                  const double* sink, double scale, double* out, double* lse,
+                                  int32_t nthreads)
 {
     int64_t n_units, u;
     int32_t group;
@@ -190,14 +206,25 @@ int oracle_attn_prefill_varlen_lse(const double* q, const double* k, const doubl
         int64_t i;
         for (i = 0; i < sq; ++i) {
             int64_t tok = cu_seqlens_q[b] + i;
-            attend_row(q + (tok * h_q + h) * d, kh, vh, d, skv, past_len[b], i, window, s,
-                       scale, score, out + (tok * h_q + h) * d,
+            attend_row(q + (tok * h_q + h) * d, kh, vh, d, skv, past_len[b], i, window,
+                       causal != 0, s, scale, score, out + (tok * h_q + h) * d,
                        lse ? lse + tok * h_q + h : NULL);
         }
         free(score);
     }
     (void)nthreads;
     return 0;
+}
+
+/* Causal, with the log-sum-exp output. */
+int oracle_attn_prefill_varlen_lse(const double* q, const double* k, const double* v,
+                                   int32_t batch, const int32_t* cu_seqlens_q,
+                                   const int32_t* past_len, int32_t h_q, int32_t h_kv, int32_t d,
+                                   int32_t s_cap, int32_t window, const double* sink,
+                                   double scale, double* out, double* lse, int32_t nthreads)
+{
+    return oracle_attn_prefill_varlen_ex(q, k, v, batch, cu_seqlens_q, past_len, h_q, h_kv, d,
+                                         s_cap, window, 1, sink, scale, out, lse, nthreads);
 }
 
 /* The same without the log-sum-exp output. */
@@ -247,7 +274,7 @@ int oracle_attn_rows_lse(const double* q, const double* k, const double* v,
             const double* kh = k + (((int64_t)b * h_kv + g) * s_cap) * d;
             const double* vh = v + (((int64_t)b * h_kv + g) * s_cap) * d;
             double* score = (double*)malloc(sizeof(double) * (size_t)(skv > 0 ? skv : 1));
-            attend_row(q + (tok * h_q + h) * d, kh, vh, d, skv, past_len[b], i, window,
+            attend_row(q + (tok * h_q + h) * d, kh, vh, d, skv, past_len[b], i, window, 1,
                        sink ? sink[h] : -INFINITY, scale, score, out_rows + r * d,
                        lse_rows ? lse_rows + r : NULL);
             free(score);
