@@ -258,7 +258,7 @@ def _split_args(torch, binding, inp, case, cu, past, window, out, n_split, ws):
             ctypes.c_void_p(inp["v_cache"].data_ptr()), cu_a, past_a, len(past), window,
             ctypes.c_void_p(inp["sink"].data_ptr()), ctypes.c_float(case.scale),
             ctypes.c_void_p(out.data_ptr()), None, inp["q"].shape[1], h_kv, d, s_cap,
-            code[inp["q"].dtype], code[out.dtype], n_split, ctypes.c_void_p(ws.data_ptr()),
+            code[inp["q"].dtype], code[out.dtype], n_split, 0, ctypes.c_void_p(ws.data_ptr()),
             ws.numel(), None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
 

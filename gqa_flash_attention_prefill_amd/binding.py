@@ -16,6 +16,7 @@ LIB_PATH = os.environ.get("ATTN_PREFILL_LIB") or os.path.join(_HERE, "libattn_pr
 
 ATTN_OK, ATTN_DECLINED, ATTN_EINVAL, ATTN_EHIP = 0, -1, -2, -3
 ATTN_F16, ATTN_BF16, ATTN_F32 = 1, 2, 3
+ATTN_FLAG_NONCAUSAL = 1
 ATTN_LOG_FIELDS = 8
 LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last",
               "n_visited")
@@ -69,8 +70,8 @@ def lib():
     L.attn_prefill_varlen.restype = ctypes.c_int
     L.attn_prefill_split.argtypes = [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp,
                                      ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                     _i32, _i32, _vp, ctypes.c_int64, ctypes.POINTER(TileLog),
-                                     _vp]
+                                     _i32, _i32, _i32, _vp, ctypes.c_int64,
+                                     ctypes.POINTER(TileLog), _vp]
     L.attn_prefill_split.restype = ctypes.c_int
     L.attn_split_workspace_bytes.argtypes = [ctypes.c_int64, _i32, _i32, _i32]
     L.attn_split_workspace_bytes.restype = ctypes.c_int64
@@ -182,10 +183,11 @@ def attn_split_workspace_bytes(q_tokens, h_q, d, n_split):
 
 def attn_prefill_split(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head_sink, scale,
                        out, lse=None, n_split=1, workspace=None, tile_log=None, stream=None,
-                       check=True):
+                       check=True, causal=True):
     """attn_prefill_varlen with a log-sum-exp side output (lse: float32 [tokens, h_q] or
-    None) and KV splits across workgroups (workspace: a device tensor of at least
-    attn_split_workspace_bytes(...) bytes when n_split > 1)."""
+    None), KV splits across workgroups (workspace: a device tensor of at least
+    attn_split_workspace_bytes(...) bytes when n_split > 1) and causal=False for
+    non-causal attention (ATTN_FLAG_NONCAUSAL)."""
     _require(q, "q", 3)
     _require(out, "out", 3)
     _require(k_cache, "k_cache", 4)
@@ -211,7 +213,8 @@ def attn_prefill_split(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head
     code = lib().attn_prefill_split(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
         float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype],
-        _DTYPE_CODE[out.dtype], int(n_split), _ptr(workspace), int(ws_bytes),
+        _DTYPE_CODE[out.dtype], int(n_split), 0 if causal else ATTN_FLAG_NONCAUSAL,
+        _ptr(workspace), int(ws_bytes),
         ctypes.byref(log) if log is not None else None, _stream(stream))
     if check:
         _check(code)

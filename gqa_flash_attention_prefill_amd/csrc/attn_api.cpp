@@ -69,7 +69,7 @@ int check_device(int* dev_out) {
 }
 
 // ---- tuning cache --------------------------------------------------------------
-using TuneKey = std::tuple<int, int, int, int64_t, int, int, int, int, int>;
+using TuneKey = std::tuple<int, int, int, int64_t, int, int, int, int, int, int>;
 std::mutex g_tune_mu;
 std::map<TuneKey, int> g_tune;
 int64_t g_sweeps = 0, g_tune_launches = 0;
@@ -104,6 +104,7 @@ struct Call {
   // log-sum-exp output and KV splits (attn_prefill_split); defaults: none, 1
   float* lse = nullptr;
   int32_t n_split = 1;
+  int32_t flags = 0;
   void* workspace = nullptr;
   int64_t workspace_bytes = 0;
 };
@@ -148,6 +149,7 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
   const int64_t tokens = c.cu[c.batch] - c.cu[0];
   p.n_split = c.n_split;
   p.ws_tokens = (int32_t)tokens;
+  p.causal = (c.flags & ATTN_FLAG_NONCAUSAL) ? 0 : 1;
   if (c.n_split > 1) {
     p.ws_o = static_cast<float*>(c.workspace);
     p.ws_lse = p.ws_o + (int64_t)c.n_split * tokens * c.h_q * c.d;
@@ -267,7 +269,7 @@ int choose_config(const Call& c, int* cfg) {
   }
   const int64_t tokens = c.cu[c.batch] - c.cu[0];
   TuneKey key{c.d, c.dtype, c.out_dtype, tokens, c.h_q, c.h_q / c.h_kv,
-              c.window > 0 ? c.window : 0, c.batch, c.n_split};
+              c.window > 0 ? c.window : 0, c.batch, c.n_split, c.flags};
   std::lock_guard<std::mutex> lk(g_tune_mu);
   auto it = g_tune.find(key);
   if (it != g_tune.end()) { *cfg = it->second; return ATTN_OK; }
@@ -306,6 +308,7 @@ int validate(const Call& c) {
     if (c.log->capacity < 0 || (c.log->capacity > 0 && !c.log->records))
       return fail(ATTN_EINVAL, "bad tile log");
   }
+  if (c.flags & ~ATTN_FLAG_NONCAUSAL) return fail(ATTN_EINVAL, "unknown flags 0x%x", c.flags);
   if (c.n_split < 1 || c.n_split > kMaxSplit)
     return fail(ATTN_EINVAL, "n_split %d outside 1..%d", c.n_split, kMaxSplit);
   if (c.n_split > 1 && tokens > 0) {
@@ -406,14 +409,16 @@ int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
                        int32_t window, const float* head_sink, float scale, void* out,
                        float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
-                       int32_t dtype, int32_t out_dtype, int32_t n_split, void* workspace,
-                       int64_t workspace_bytes, attn_tile_log* tile_log, void* stream) {
+                       int32_t dtype, int32_t out_dtype, int32_t n_split, int32_t flags,
+                       void* workspace, int64_t workspace_bytes, attn_tile_log* tile_log,
+                       void* stream) {
   try {
     Call c{q, k_cache, v_cache, out, head_sink, cu_seqlens_q, past_len, batch, window, h_q,
            h_kv, d, s_cap, dtype, out_dtype, scale, tile_log,
            reinterpret_cast<hipStream_t>(stream)};
     c.lse = lse;
     c.n_split = n_split;
+    c.flags = flags;
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
     return run(c);
@@ -448,7 +453,7 @@ int32_t attn_tuned_config(int32_t d, int32_t dtype, int32_t out_dtype, int64_t q
                           int32_t h_q, int32_t h_kv, int32_t window, int32_t batch) {
   if (h_kv <= 0) return -1;
   const TuneKey key{d, dtype, out_dtype, q_tokens, h_q, h_q / h_kv, window > 0 ? window : 0,
-                    batch, 1};  // the key of unsplit calls
+                    batch, 1, 0};  // the key of unsplit causal calls
   std::lock_guard<std::mutex> lk(g_tune_mu);
   auto it = g_tune.find(key);
   return it == g_tune.end() ? -1 : it->second;

@@ -39,6 +39,7 @@ struct Params {
   float* ws_lse;       // n_split > 1: partial log-sum-exp [n_split, ws_tokens, h_q] (log2 units)
   int32_t n_split;     // 1: the kernel writes `out`; > 1: it writes partials for attn merge
   int32_t ws_tokens;   // q rows of the whole call (workspace stride)
+  int32_t causal;      // 0: non-causal (split/lse kernel variant only)
   SeqTable seq;
 };
 

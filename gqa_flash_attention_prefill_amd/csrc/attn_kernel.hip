@@ -354,7 +354,10 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   // KV tiles of the whole Q tile: floor from the first row, ceiling from the last
   const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
   int t_lo = lo_key / BKV;
-  int t_hi = (past + q_last) / BKV;
+  // non-causal (split/lse variant only): every row keeps every key of its
+  // sequence above the window floor, so the ceiling is the last key's tile
+  const bool causal = !XTRA || p.causal;
+  int t_hi = (causal ? past + q_last : skv - 1) / BKV;
   if constexpr (XTRA) split_range(p, &t_lo, &t_hi);
   const int n_stages = max(0, (t_hi - t_lo + S) / S);
 
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   const int pos = q0 + row / p.hpack;
   const int head = g * p.group + hg * p.hpack + row % p.hpack;
   const bool valid = pos < sq;
-  const int row_hi = past + pos;                               // last kept key
+  const int row_hi = causal ? past + pos : skv - 1;           // last kept key
   const int row_lo = window > 0 ? past + pos - window + 1 : 0;  // first kept key
 
   // ---- this row group's rows: skip tiles none of them keeps ----
@@ -371,9 +374,9 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   const int wp1 = min(q0 + (rg * 32 + 31) / p.hpack, sq - 1);
   const bool wave_live = wp0 < sq;
   const int w_lo = window > 0 ? max(0, past + wp0 - window + 1) / BKV : 0;
-  const int w_hi = (past + wp1) / BKV;
+  const int w_hi = (causal ? past + wp1 : skv - 1) / BKV;
   const int w_full_lo = window > 0 ? past + wp1 - window + 1 : 0;  // max row lower bound
-  const int w_full_hi = past + wp0;                                 // min row upper bound
+  const int w_full_hi = causal ? past + wp0 : skv - 1;              // min row upper bound
 
   const float c = p.scale_log2;
   const float kNegInf = -__builtin_inff();
@@ -785,7 +788,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
 
   const int lo_key = window > 0 ? max(0, past + q0 - window + 1) : 0;
   int t_lo = lo_key / BKV;
-  int t_hi = (past + q_last) / BKV;
+  // non-causal (split/lse variant only): every row keeps every key of its
+  // sequence above the window floor, so the ceiling is the last key's tile
+  const bool causal = !XTRA || p.causal;
+  int t_hi = (causal ? past + q_last : skv - 1) / BKV;
   if constexpr (XTRA) split_range(p, &t_lo, &t_hi);
   const int n_stages = max(0, (t_hi - t_lo + 2) / 2);  // group 0's tiles (group 1: same or one fewer)
 
@@ -793,16 +799,16 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   const int pos = q0 + row / p.hpack;
   const int head = g * p.group + hg * p.hpack + row % p.hpack;
   const bool valid = pos < sq;
-  const int row_hi = past + pos;
+  const int row_hi = causal ? past + pos : skv - 1;
   const int row_lo = window > 0 ? past + pos - window + 1 : 0;
 
   const int wp0 = q0 + (rg * 32) / p.hpack;
   const int wp1 = min(q0 + (rg * 32 + 31) / p.hpack, sq - 1);
   const bool wave_live = wp0 < sq;
   const int w_lo = window > 0 ? max(0, past + wp0 - window + 1) / BKV : 0;
-  const int w_hi = (past + wp1) / BKV;
+  const int w_hi = (causal ? past + wp1 : skv - 1) / BKV;
   const int w_full_lo = window > 0 ? past + wp1 - window + 1 : 0;
-  const int w_full_hi = past + wp0;
+  const int w_full_hi = causal ? past + wp0 : skv - 1;
 
   const float c = p.scale_log2;
   const float kNegInf = -__builtin_inff();
@@ -1170,7 +1176,7 @@ void launch_pp_x(const Params& p, int n_items, hipStream_t stream) {
 
 template <int D, int BKV, int NS, typename TI, typename TO>
 hipError_t launch_pp(const Params& p, int n_items, hipStream_t stream) {
-  if (p.n_split > 1 || p.lse != nullptr)
+  if (p.n_split > 1 || p.lse != nullptr || !p.causal)
     launch_pp_x<D, BKV, NS, true, TI, TO>(p, n_items, stream);
   else
     launch_pp_x<D, BKV, NS, false, TI, TO>(p, n_items, stream);
@@ -1191,7 +1197,7 @@ void launch_x(const Params& p, int n_items, hipStream_t stream) {
 
 template <int D, int BKV, int R, int S, int NS, typename TI, typename TO>
 hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
-  if (p.n_split > 1 || p.lse != nullptr)
+  if (p.n_split > 1 || p.lse != nullptr || !p.causal)
     launch_x<D, BKV, R, S, NS, true, TI, TO>(p, n_items, stream);
   else
     launch_x<D, BKV, R, S, NS, false, TI, TO>(p, n_items, stream);

@@ -65,6 +65,7 @@ extern "C" {
 
 enum { ATTN_OK = 0, ATTN_DECLINED = -1, ATTN_EINVAL = -2, ATTN_EHIP = -3 };
 enum { ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_F32 = 3 };
+enum { ATTN_FLAG_NONCAUSAL = 1 };  /* attn_prefill_split flags */
 
 /* Fields of one visited-tile record (int32 each). */
 enum {
@@ -151,6 +152,12 @@ int attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
  *                attn_split_workspace_bytes(tokens, h_q, d, n_split) bytes when
  *                n_split > 1 (caller-owned; the call overwrites it; calls that
  *                share one workspace must be ordered on one stream).
+ *   flags        0, or ATTN_FLAG_NONCAUSAL: every row keeps every key of its
+ *                sequence, k < past_len + sq, still above the window's floor
+ *                when window > 0 (sglang pull request 34468 tests its kernel
+ *                "causal and non-causal"; reading: the window's lower bound is
+ *                a mask of its own).  The KV loop then ends at the sequence's
+ *                last key's tile for every Q tile.
  *   tile_log     records per (work item, split): the split's own tile range.
  * Errors as attn_prefill_varlen; -2 also for n_split outside 1..64 or a
  * missing / too small workspace, -1 for a misaligned workspace.
@@ -159,8 +166,9 @@ int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
                        int32_t window, const float* head_sink, float scale, void* out,
                        float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
-                       int32_t dtype, int32_t out_dtype, int32_t n_split, void* workspace,
-                       int64_t workspace_bytes, attn_tile_log* tile_log, void* stream);
+                       int32_t dtype, int32_t out_dtype, int32_t n_split, int32_t flags,
+                       void* workspace, int64_t workspace_bytes, attn_tile_log* tile_log,
+                       void* stream);
 
 /* Bytes of workspace attn_prefill_split needs (0 for n_split = 1; -1 for
  * invalid sizes): n_split * q_tokens * h_q * (d + 1) * 4. */

@@ -123,10 +123,10 @@ def test_split_entry_validates_before_any_gpu_call():
     past = (ctypes.c_int32 * 1)(0)
     fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
 
-    def call(n_split, ws, ws_bytes):
+    def call(n_split, ws, ws_bytes, flags=0):
         return L.attn_prefill_split(fake, fake, fake, cu, past, 1, -1, None, ctypes.c_float(0.125),
                                     fake, None, 8, 2, 64, 64, binding.ATTN_F16, binding.ATTN_F16,
-                                    n_split, ws, ws_bytes, None, None)
+                                    n_split, flags, ws, ws_bytes, None, None)
 
     need = binding.attn_split_workspace_bytes(64, 8, 64, 4)
     assert need == 4 * 64 * 8 * 65 * 4
@@ -138,3 +138,5 @@ def test_split_entry_validates_before_any_gpu_call():
     assert call(4, fake, need - 4) == binding.ATTN_EINVAL
     assert "workspace" in binding.attn_last_error()
     assert call(4, ctypes.c_void_p(0x10004), need) == binding.ATTN_DECLINED
+    assert call(1, None, 0, flags=2) == binding.ATTN_EINVAL
+    assert "flags" in binding.attn_last_error()
