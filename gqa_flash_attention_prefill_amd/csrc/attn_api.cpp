@@ -128,7 +128,7 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
   const int group = c.h_q / c.h_kv;
   const int hpack = gcd_int(group, 32);
   const int q_rows = cfg.rows / hpack;
-  attn::LaunchFn fn = cfg.fn[c.d == 128][c.dtype == ATTN_BF16][c.out_dtype == ATTN_F32];
+  attn::LaunchFn fn = cfg.fn[attn::d_index(c.d)][c.dtype == ATTN_BF16][c.out_dtype == ATTN_F32];
 
   attn::Params p;
   memset(&p, 0, sizeof(p));
@@ -318,7 +318,8 @@ int validate(const Call& c) {
                   (long long)c.workspace_bytes, (long long)need);
   }
   // declines: valid requests this library does not implement
-  if (c.d != 64 && c.d != 128) return fail(ATTN_DECLINED, "d=%d not supported (64, 128)", c.d);
+  if (c.d != 64 && c.d != 128 && c.d != 256)
+    return fail(ATTN_DECLINED, "d=%d not supported (64, 128, 256)", c.d);
   if (c.dtype != ATTN_F16 && c.dtype != ATTN_BF16)
     return fail(ATTN_DECLINED, "input dtype %d not supported", c.dtype);
   if (c.out_dtype != c.dtype && c.out_dtype != ATTN_F32)
@@ -356,7 +357,7 @@ int run(const Call& c) {
       return fail(ATTN_EINVAL, "tile log holds %lld records, %lld needed",
                   (long long)c.log->capacity, (long long)need);
     log_base = c.log->records;
-    c.log->bkv = attn::config(cfg).bkv[c.d == 128];
+    c.log->bkv = attn::config(cfg).bkv[attn::d_index(c.d)];
     const int hpack = gcd_int(c.h_q / c.h_kv, 32);
     c.log->q_rows = attn::config(cfg).rows / hpack;
   }

@@ -61,11 +61,14 @@ using LaunchFn = hipError_t (*)(const Params&, int n_items, hipStream_t);
 
 struct KernelConfig {
   const char* name;
-  int bkv[2];     // keys per KV tile, [d == 128]
+  int bkv[3];     // keys per KV tile, [d_index(d)]
   int rows;       // Q-tile rows (q positions x packed heads)
-  // indexed [d == 128][dtype == bf16][out is f32]
-  LaunchFn fn[2][2][2];
+  // indexed [d_index(d)][dtype == bf16][out is f32]
+  LaunchFn fn[3][2][2];
 };
+
+// 0: d 64, 1: d 128, 2: d 256
+inline int d_index(int d) { return d == 64 ? 0 : (d == 128 ? 1 : 2); }
 
 int config_count();
 const KernelConfig& config(int i);

@@ -134,7 +134,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 //     instruction its own banks.
 template <int D>
 __device__ inline int k_chunk(int key, int c) {
-  return D == 64 ? c ^ ((key >> 1) & 7) : c ^ (key & 15);
+  return D == 64 ? c ^ ((key >> 1) & 7) : c ^ (key & 15);   // d 256: rows span two bank widths
 }
 template <int D>
 __device__ inline int v_chunk(int key, int c) {
@@ -298,9 +298,10 @@ __device__ inline void split_range(const Params& p, int* t_lo, int* t_hi) {
 // so matrix and vector work of neighbouring tiles overlap inside the wave.
 template <int D, int BKV, int R, int S_REQ, int NSLOT, bool WIN, bool XTRA, typename TI,
           typename TO>
-__global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kernel(Params p) {
-  // stages of two 64-key d=128 tiles would not fit in LDS: d=128 uses one split
-  constexpr int S = (D == 128) ? 1 : S_REQ;
+__global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kernel(Params p) {
+  // stages of two 64-key d=128 tiles would not fit in LDS: d >= 128 uses one
+  // split (and d = 256 32-key tiles, chosen by its launcher)
+  constexpr int S = (D >= 128) ? 1 : S_REQ;
   constexpr int NW = R * S;
   constexpr int NT = NW * 64;
   static_assert(NSLOT == 3 || NSLOT == 4, "LDS ring of 3 or 4 stages");
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(R * (D == 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   constexpr int NG = BKV / 16;              // 16-key PV steps per KV tile
   constexpr int DB = D / 32;                // 32-wide d blocks of the output
   constexpr float kRescale = 8.f;           // lazy-rescale threshold (log2 units)
-  static_assert(BKV % 32 == 0 && (D == 64 || D == 128), "tile shape");
+  static_assert(BKV % 32 == 0 && (D == 64 || D == 128 || D == 256), "tile shape");
   static_assert(S == 1 || S == 2, "1 or 2 KV splits");
 
   __shared__ u32x4 lds[NSLOT * STAGE_CH];
@@ -1186,7 +1187,7 @@ hipError_t launch_pp(const Params& p, int n_items, hipStream_t stream) {
 
 template <int D, int BKV, int R, int S, int NS, bool XTRA, typename TI, typename TO>
 void launch_x(const Params& p, int n_items, hipStream_t stream) {
-  constexpr int threads = R * (D == 128 ? 1 : S) * 64;
+  constexpr int threads = R * (D >= 128 ? 1 : S) * 64;
   if (p.window > 0)
     hipLaunchKernelGGL((attn_fwd_kernel<D, BKV, R, S, NS, true, XTRA, TI, TO>),
                        dim3(n_items, p.n_split), dim3(threads), 0, stream, p);
@@ -1204,14 +1205,17 @@ hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// d = 256 runs 32-key tiles (a stage of 64-key d 256 K and V tiles is 64 KB)
 template <int BKV, int R, int S, int NS = 3>
 constexpr KernelConfig make_config(const char* name) {
   return KernelConfig{
-      name, {BKV, BKV}, R * 32,
+      name, {BKV, BKV, 32}, R * 32,
       {{{launch<64, BKV, R, S, NS, F16, uint16_t>, launch<64, BKV, R, S, NS, F16, float>},
         {launch<64, BKV, R, S, NS, BF16, uint16_t>, launch<64, BKV, R, S, NS, BF16, float>}},
        {{launch<128, BKV, R, S, NS, F16, uint16_t>, launch<128, BKV, R, S, NS, F16, float>},
-        {launch<128, BKV, R, S, NS, BF16, uint16_t>, launch<128, BKV, R, S, NS, BF16, float>}}}};
+        {launch<128, BKV, R, S, NS, BF16, uint16_t>, launch<128, BKV, R, S, NS, BF16, float>}},
+       {{launch<256, 32, R, S, NS, F16, uint16_t>, launch<256, 32, R, S, NS, F16, float>},
+        {launch<256, 32, R, S, NS, BF16, uint16_t>, launch<256, 32, R, S, NS, BF16, float>}}}};
 }
 
 // ---------------------------------------------------------------------------
@@ -1270,17 +1274,19 @@ hipError_t launch_merge_t(const MergeParams& mp, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Ping-pong configuration for d = 64; at d = 128 (where its register budget
-// does not hold two groups' fragments) the same entry runs the split-free
-// kernel with the same 128-row Q tiles.
+// Ping-pong configuration for d = 64; at d = 128 and 256 (where its register
+// budget does not hold two groups' fragments) the same entry runs the
+// split-free kernel with the same 128-row Q tiles.
 template <int BKV, int NS>
 constexpr KernelConfig make_pp_config(const char* name) {
   return KernelConfig{
-      name, {BKV, 64}, 128,
+      name, {BKV, 64, 32}, 128,
       {{{launch_pp<64, BKV, NS, F16, uint16_t>, launch_pp<64, BKV, NS, F16, float>},
         {launch_pp<64, BKV, NS, BF16, uint16_t>, launch_pp<64, BKV, NS, BF16, float>}},
        {{launch<128, 64, 4, 1, 3, F16, uint16_t>, launch<128, 64, 4, 1, 3, F16, float>},
-        {launch<128, 64, 4, 1, 3, BF16, uint16_t>, launch<128, 64, 4, 1, 3, BF16, float>}}}};
+        {launch<128, 64, 4, 1, 3, BF16, uint16_t>, launch<128, 64, 4, 1, 3, BF16, float>}},
+       {{launch<256, 32, 4, 1, 3, F16, uint16_t>, launch<256, 32, 4, 1, 3, F16, float>},
+        {launch<256, 32, 4, 1, 3, BF16, uint16_t>, launch<256, 32, 4, 1, 3, BF16, float>}}}};
 }
 
 const KernelConfig kConfigs[] = {
@@ -1304,9 +1310,13 @@ hipError_t launch_merge(const MergeParams& mp, int out_is_f32, int out_is_bf16,
     return out == 2 ? launch_merge_t<64, 2>(mp, stream)
                     : (out == 1 ? launch_merge_t<64, 1>(mp, stream)
                                 : launch_merge_t<64, 0>(mp, stream));
-  return out == 2 ? launch_merge_t<128, 2>(mp, stream)
-                  : (out == 1 ? launch_merge_t<128, 1>(mp, stream)
-                              : launch_merge_t<128, 0>(mp, stream));
+  if (mp.d == 128)
+    return out == 2 ? launch_merge_t<128, 2>(mp, stream)
+                    : (out == 1 ? launch_merge_t<128, 1>(mp, stream)
+                                : launch_merge_t<128, 0>(mp, stream));
+  return out == 2 ? launch_merge_t<256, 2>(mp, stream)
+                  : (out == 1 ? launch_merge_t<256, 1>(mp, stream)
+                              : launch_merge_t<256, 0>(mp, stream));
 }
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

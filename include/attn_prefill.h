@@ -43,7 +43,7 @@
  *    for a new tuning key, which runs a synchronous tuning sweep on that
  *    stream (see attn_tune_stats).
  *  - Return codes: ATTN_OK; ATTN_DECLINED (-1): the request is valid but not
- *    supported (d not 64/128, dtype not f16/bf16, out dtype neither the input
+ *    supported (d not 64/128/256, dtype not f16/bf16, out dtype neither the input
  *    dtype nor f32, misaligned pointers, device not gfx950) -- nothing is
  *    launched and out is untouched, so the caller can fall back; ATTN_EINVAL
  *    (-2): invalid arguments (null pointers, non-positive sizes, h_q not a

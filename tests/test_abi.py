@@ -59,7 +59,7 @@ def _varlen(L, cu, past, *, window=-1, h_q=8, h_kv=2, d=64, s_cap=64, log=None, 
     (dict(h_q=0), binding.ATTN_EINVAL),
     (dict(scale=float("nan")), binding.ATTN_EINVAL),
     (dict(d=96), binding.ATTN_DECLINED),                  # head dim not implemented
-    (dict(d=256), binding.ATTN_DECLINED),
+    (dict(d=512), binding.ATTN_DECLINED),                 # head dim not implemented
     (dict(dtype=3, out_dtype=3), binding.ATTN_DECLINED),  # f32 inputs
     (dict(dtype=1, out_dtype=2), binding.ATTN_DECLINED),  # f16 in, bf16 out
     (dict(q=MISALIGNED), binding.ATTN_DECLINED),
