@@ -229,6 +229,41 @@ def summarize_counters(fetch_dir, write_dir):
     return res
 
 
+def summarize_pmc(d):
+    """Mean over dispatches of each counter (summed over its instances) for the
+    attention kernels of a rocprofv3 --pmc run."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if _classify(r["Kernel_Name"]) not in ("attn_full", "attn_window"):
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _, counter), v in per.items():
+        out.setdefault(name, {}).setdefault(counter, []).append(v)
+    return {name: {c: {"mean": sum(v) / len(v), "dispatches": len(v)} for c, v in cs.items()}
+            for name, cs in out.items()}
+
+
+def one_call(torch, binding, chunk):
+    """Three untimed launches of one full-attention call shape (chunk `chunk`
+    of the 16k prefill: 512 rows after 512 * chunk cached keys) on layer 0's
+    buffers, for hardware-counter passes on that shape alone."""
+    from gqa_flash_attention_prefill_amd import synth
+    torch.cuda.set_device(0)
+    case = synth.chunked16k_layer(0)
+    inp = synth.make(case, device="cuda:0")
+    out = torch.empty_like(inp["q"])
+    q = inp["q"][chunk * CHUNK:(chunk + 1) * CHUNK]
+    o = out[chunk * CHUNK:(chunk + 1) * CHUNK]
+    for _ in range(3):
+        binding.attn_prefill(q, inp["k_cache"], inp["v_cache"], chunk * CHUNK, case.window,
+                             inp["sink"], case.scale, o)
+    torch.cuda.synchronize()
+    print(f"[bench] one_call chunk {chunk}: 3 launches of the full-attention call", flush=True)
+
+
 def _time_calls(torch, binding, args, reps=20):
     """Mean us per call of `reps` back-to-back attn_prefill_split calls with
     pre-marshalled arguments, between one event pair on the launch stream
@@ -334,9 +369,17 @@ def main():
     ap.add_argument("--summarize-trace", default=None, metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-counters", nargs=2, default=None,
                     metavar=("FETCH_SIZE_DIR", "WRITE_SIZE_DIR"))
+    ap.add_argument("--one-call", type=int, default=None, metavar="CHUNK",
+                    help="only run the full-attention call of chunk CHUNK (3 times, untimed), "
+                         "for hardware-counter passes on one launch shape")
+    ap.add_argument("--summarize-pmc", default=None, metavar="PMC_DIR",
+                    help="per-dispatch averages of every counter of the attention kernels")
     args = ap.parse_args()
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
         return
     if args.summarize_counters:
         res = summarize_counters(*args.summarize_counters)
@@ -351,6 +394,9 @@ def main():
     import torch
     from gqa_flash_attention_prefill_amd import binding
     L = binding.lib()
+    if args.one_call is not None:
+        one_call(torch, binding, args.one_call)
+        return
     if args.split_demo or args.decode_demo:
         torch.cuda.set_device(0)
         demo = split_demo if args.split_demo else decode_demo

@@ -927,40 +927,49 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   };
   // M_j: S_{j+1} = K_{j+1} . Q^T from kf and O^T += V_j^T . P_j^T from vf,
   // refilling each fragment register from the next tile (kf <- K_{j+2},
-  // vf <- V_{j+1}) right after the MFMA that last reads it.  One or two LDS
-  // reads between consecutive MFMAs keep this wave's issue slots busy while
-  // the matrix pipe runs, without the read bursts that overflow the LDS
-  // command queue (four waves of a CU are in this phase at once).
+  // vf <- V_{j+1}).  Each read follows the MFMA after the one that last reads
+  // the register it refills, so a load never targets an operand of the MFMA
+  // just issued; one or two LDS reads between consecutive MFMAs keep this
+  // wave's issue slots busy while the matrix pipe runs, without the read
+  // bursts that overflow the LDS command queue (four waves of a CU are in
+  // this phase at once).
   auto m_phase = [&](int j) {
     const u32x4* kt = ring + ((j + 2) % NS) * SLOT_CH;
     const u32x4* vt = ring + ((j + 1) % NS) * SLOT_CH + TILE_CH;
+    constexpr int kMfma = 0x008, kDsRead = 0x100;
+    constexpr int PVM = TI::kSplitP ? 2 : 1;   // MFMAs per P.V step
+    auto refill_k = [&](int i) {
+      const int kk = i / NB, nb = i % NB;
+      const int kr = nb * 32 + col;
+      kf[nb][kk] = kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)];
+    };
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if (kk == 0)
-          sc[nb] = TI::mma(kf[nb][0], qf[0], TI::kPrescaleQ ? (nb ? negm1 : negm) : f32x16{});
-        else
-          sc[nb] = TI::mma(kf[nb][kk], qf[kk], sc[nb]);
-        const int kr = nb * 32 + col;
-        kf[nb][kk] = kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)];
-      }
+    for (int i = 0; i < NB * KSTEPS; ++i) {
+      const int kk = i / NB, nb = i % NB;
+      if (kk == 0)
+        sc[nb] = TI::mma(kf[nb][0], qf[0], TI::kPrescaleQ ? (nb ? negm1 : negm) : f32x16{});
+      else
+        sc[nb] = TI::mma(kf[nb][kk], qf[kk], sc[nb]);
+      if (i > 0) refill_k(i - 1);   // the previous MFMA's operand, never the one in flight
+    }
 #pragma unroll
     for (int g16 = 0; g16 < NG; ++g16) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         acc[db] = TI::mma(vf[db][g16], pb[g16], acc[db]);
         if constexpr (TI::kSplitP) acc[db] = TI::mma(vf[db][g16], pl[g16], acc[db]);
-        vf[db][g16] = v_frag<D>(vt, g16, db, lane);
+        if (g16 == 0 && db == 0) refill_k(NB * KSTEPS - 1);
+        else if (db > 0) vf[db - 1][g16] = v_frag<D>(vt, g16, db - 1, lane);
       }
       lsum = TI::mma(ones, pb[g16], lsum);
       if constexpr (TI::kSplitP) lsum = TI::mma(ones, pl[g16], lsum);
+      vf[DB - 1][g16] = v_frag<D>(vt, g16, DB - 1, lane);
     }
-    // issue order: (MFMA, read) x NB*KSTEPS, then per 16-key step
-    // (MFMA, 2 reads) x DB and the row-sum MFMA
-    constexpr int kMfma = 0x008, kDsRead = 0x100;
+    // issue order as written: each read follows the MFMA after the one that
+    // last reads the register it refills
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
 #pragma unroll
-    for (int i = 0; i < NB * KSTEPS; ++i) {
+    for (int i = 1; i < NB * KSTEPS; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
     }
@@ -968,10 +977,12 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     for (int g16 = 0; g16 < NG; ++g16) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, TI::kSplitP ? 2 : 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kMfma, PVM, 0);
+        if (g16 == 0 && db == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        else if (db > 0) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kMfma, TI::kSplitP ? 2 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kMfma, PVM, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
     }
   };
   auto make_p = [&]() {
