@@ -353,6 +353,74 @@ def decode_demo(torch, binding):
                         "H_kv 8, d 64, fp16, sinks", "results": res}
 
 
+def paged_demo(torch, binding):
+    """The token-pool layout against dense caches on the same keys: every
+    key row moved to a random row of a pool [n_pool, H_kv, d] (no two
+    consecutive keys adjacent), addressed through kv_indices.  Two calls:
+    the deepest full-attention chunk of the 16k prefill (512 rows after 15872
+    keys) and a 64-sequence decode step (one row after 16383 keys each),
+    H_q 64 / H_kv 8, d 64, fp16, sinks.  Mean of 20 back-to-back calls each;
+    the dense split entry with an lse output runs the same kernel variant as
+    the pool call, the plain dense call the variant without the options."""
+    from gqa_flash_attention_prefill_amd import synth
+    L = binding.lib()
+    res = []
+    for label, nseq, past, sq in (("chunk31_full", 1, 15872, 512), ("decode64_full", 64, 16383, 1)):
+        case = synth.Case(label, h_q=H_Q, h_kv=H_KV, d=D, sq=[sq] * nseq, past=[past] * nseq,
+                          window=-1, seed=79, poison_tail=False)
+        inp = synth.make(case, device="cuda")
+        tokens = sq * nseq
+        skv = past + sq
+        out = torch.empty_like(inp["q"])
+        lse = torch.empty((tokens, H_Q), dtype=torch.float32, device="cuda")
+        g = torch.Generator(device="cpu").manual_seed(80)
+        n_pool = nseq * skv
+        rows = torch.randperm(n_pool, generator=g).to(torch.int32)
+        k_pool = torch.empty((n_pool, H_KV, D), dtype=torch.float16, device="cuda")
+        v_pool = torch.empty_like(k_pool)
+        rows_d = rows.to("cuda")
+        for b in range(nseq):
+            r = rows_d[b * skv:(b + 1) * skv].long()
+            k_pool[r] = inp["k_cache"][b, :, :skv, :].transpose(0, 1)
+            v_pool[r] = inp["v_cache"][b, :, :skv, :].transpose(0, 1)
+        cu = (ctypes.c_int32 * (nseq + 1))(*[sq * i for i in range(nseq + 1)])
+        pl = (ctypes.c_int32 * nseq)(*([past] * nseq))
+        ip = (ctypes.c_int32 * (nseq + 1))(*[skv * i for i in range(nseq + 1)])
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        f16 = binding.ATTN_F16
+        s_cap = inp["k_cache"].shape[2]
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        dense = (vp(inp["q"]), vp(inp["k_cache"]), vp(inp["v_cache"]), cu, pl, nseq, -1,
+                 vp(inp["sink"]), ctypes.c_float(case.scale), vp(out), H_Q, H_KV, D, s_cap, f16,
+                 f16, None, st)
+        dense_lse = (vp(inp["q"]), vp(inp["k_cache"]), vp(inp["v_cache"]), cu, pl, nseq, -1,
+                     vp(inp["sink"]), ctypes.c_float(case.scale), vp(out), vp(lse), H_Q, H_KV, D,
+                     s_cap, f16, f16, 1, 0, None, 0, None, st)
+        pool = (vp(inp["q"]), vp(k_pool), vp(v_pool), n_pool, vp(rows_d), ip, cu, pl, nseq, -1,
+                vp(inp["sink"]), ctypes.c_float(case.scale), vp(out), vp(lse), H_Q, H_KV, D, f16,
+                f16, 0, None, st)
+        row = {"call": label}
+        for name, fn, a in (("dense", L.attn_prefill_varlen, dense),
+                            ("dense_lse", L.attn_prefill_split, dense_lse),
+                            ("pool_lse", L.attn_prefill_paged, pool)):
+            for _ in range(3):
+                if fn(*a) != 0:
+                    raise RuntimeError(binding.attn_last_error())
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn(*a)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 20
+            fl = 4.0 * D * H_Q * nseq * sum(past + i + 1 for i in range(sq))
+            row[name] = {"us": round(us, 2), "tflops": round(fl / us / 1e6, 1)}
+        res.append(row)
+    return {"workload": "token pool (keys scattered to random pool rows) vs dense caches, "
+                        "H_q 64 / H_kv 8, d 64, fp16, sinks, full attention", "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +431,8 @@ def main():
                     help="time a 64-sequence decode step (prints its own JSON line)")
     ap.add_argument("--split-demo", action="store_true",
                     help="time KV splits on a few-Q-tile call (prints its own JSON line)")
+    ap.add_argument("--paged-demo", action="store_true",
+                    help="time the token-pool layout against dense caches (prints its own JSON line)")
     ap.add_argument("--detail", default=None, help="write per-chunk timings (JSON) here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run the 1 GiB cold copy used to scale HBM counters")
@@ -397,9 +467,9 @@ def main():
     if args.one_call is not None:
         one_call(torch, binding, args.one_call)
         return
-    if args.split_demo or args.decode_demo:
+    if args.split_demo or args.decode_demo or args.paged_demo:
         torch.cuda.set_device(0)
-        demo = split_demo if args.split_demo else decode_demo
+        demo = split_demo if args.split_demo else (decode_demo if args.decode_demo else paged_demo)
         print(json.dumps(demo(torch, binding)), flush=True)
         return
     dev = "cuda:0"

@@ -23,7 +23,7 @@ LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last
 
 _DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
 
-EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_split",
+EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_split", "attn_prefill_paged",
             "attn_split_workspace_bytes", "attn_last_error", "attn_tune_stats",
             "attn_tune_reset", "attn_tuned_config", "attn_config_count", "attn_config_name",
             "attn_force_config")
@@ -73,6 +73,10 @@ def lib():
                                      _i32, _i32, _i32, _vp, ctypes.c_int64,
                                      ctypes.POINTER(TileLog), _vp]
     L.attn_prefill_split.restype = ctypes.c_int
+    L.attn_prefill_paged.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _vp, _i32p, _i32p, _i32p,
+                                     _i32, _i32, _vp, ctypes.c_float, _vp, _vp, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, ctypes.POINTER(TileLog), _vp]
+    L.attn_prefill_paged.restype = ctypes.c_int
     L.attn_split_workspace_bytes.argtypes = [ctypes.c_int64, _i32, _i32, _i32]
     L.attn_split_workspace_bytes.restype = ctypes.c_int64
     L.attn_last_error.argtypes = []
@@ -215,6 +219,49 @@ def attn_prefill_split(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head
         float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype],
         _DTYPE_CODE[out.dtype], int(n_split), 0 if causal else ATTN_FLAG_NONCAUSAL,
         _ptr(workspace), int(ws_bytes),
+        ctypes.byref(log) if log is not None else None, _stream(stream))
+    if check:
+        _check(code)
+    if log is not None:
+        return code, log.n_records, log.bkv, log.q_rows
+    return code
+
+
+def attn_prefill_paged(q, k_pool, v_pool, kv_indices, kv_indptr, cu_seqlens_q, past_len, window,
+                       head_sink, scale, out, lse=None, tile_log=None, stream=None, check=True,
+                       causal=True):
+    """Ragged batch over a token pool: k_pool / v_pool [n_pool, h_kv, d];
+    kv_indices an int32 device tensor of pool rows; kv_indptr, cu_seqlens_q and
+    past_len host sequences of ints (key k of sequence b is pool row
+    kv_indices[kv_indptr[b] + k])."""
+    _require(q, "q", 3)
+    _require(out, "out", 3)
+    _require(k_pool, "k_pool", 3)
+    _require(v_pool, "v_pool", 3)
+    tokens, h_q, d = q.shape
+    n_pool, h_kv, _ = k_pool.shape
+    nseq = len(past_len)
+    if len(cu_seqlens_q) != nseq + 1 or len(kv_indptr) != nseq + 1:
+        raise ValueError("cu_seqlens_q and kv_indptr must have len(past_len) + 1 entries")
+    if kv_indices.dtype != torch.int32 or not kv_indices.is_contiguous():
+        raise ValueError("kv_indices must be a contiguous int32 tensor")
+    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
+    ip = (ctypes.c_int32 * len(kv_indptr))(*[int(x) for x in kv_indptr])
+    pl = (ctypes.c_int32 * max(1, nseq))(*[int(x) for x in past_len])
+    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
+        raise ValueError("head_sink must be a contiguous float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (tokens, h_q)):
+        raise ValueError("lse must be a contiguous float32 tensor [tokens, h_q]")
+    log = None
+    if tile_log is not None:
+        if tile_log.dtype != torch.int32 or tile_log.dim() != 2 or tile_log.shape[1] != 8:
+            raise ValueError("tile_log must be an int32 tensor [capacity, 8]")
+        log = TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
+    code = lib().attn_prefill_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), int(n_pool), _ptr(kv_indices), ip, cu, pl, nseq,
+        int(window), _ptr(head_sink), float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d,
+        _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], 0 if causal else ATTN_FLAG_NONCAUSAL,
         ctypes.byref(log) if log is not None else None, _stream(stream))
     if check:
         _check(code)

@@ -107,6 +107,10 @@ struct Call {
   int32_t flags = 0;
   void* workspace = nullptr;
   int64_t workspace_bytes = 0;
+  // token-pool layout (attn_prefill_paged): k / v are pools [n_pool, h_kv, d]
+  const int32_t* kv_idx = nullptr;     // device: pool row of each key
+  const int32_t* kv_indptr = nullptr;  // host [batch + 1]: sequence b's entries in kv_idx
+  int64_t n_pool = 0;
 };
 
 constexpr int32_t kMaxSplit = 64;
@@ -150,6 +154,11 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
   p.n_split = c.n_split;
   p.ws_tokens = (int32_t)tokens;
   p.causal = (c.flags & ATTN_FLAG_NONCAUSAL) ? 0 : 1;
+  if (c.kv_idx) {
+    p.kv_idx = c.kv_idx;
+    p.kv_row_bytes = (uint32_t)((int64_t)c.h_kv * c.d * 2);
+    p.n_pool = (uint32_t)c.n_pool;
+  }
   if (c.n_split > 1) {
     p.ws_o = static_cast<float*>(c.workspace);
     p.ws_lse = p.ws_o + (int64_t)c.n_split * tokens * c.h_q * c.d;
@@ -170,6 +179,7 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
       st.cu_q[i + 1] = c.cu[b0 + i + 1];
       st.past[i] = c.past[b0 + i];
       st.slot[i] = b0 + i;
+      st.kv_start[i] = c.kv_indptr ? c.kv_indptr[b0 + i] : 0;
     }
     const int64_t n_items = (int64_t)st.cu_tiles[nb] * c.h_kv * p.n_hgroups;
     if (n_items == 0) continue;
@@ -222,7 +232,9 @@ int sweep(const Call& c_in, int* best_out) {
   std::vector<int32_t> deep(c_in.batch > 0 ? c_in.batch : 1);
   for (int32_t b = 0; b < c_in.batch; ++b) {
     const int32_t sq = c_in.cu[b + 1] - c_in.cu[b];
-    deep[b] = std::max(c_in.past[b], std::min(c_in.s_cap, kSweepDepth) - sq);
+    // a token-pool call's index lists end at its own keys: no deeper sample
+    deep[b] = c_in.kv_idx ? c_in.past[b]
+                          : std::max(c_in.past[b], std::min(c_in.s_cap, kSweepDepth) - sq);
   }
   Call c = c_in;
   c.past = deep.data();
@@ -269,7 +281,8 @@ int choose_config(const Call& c, int* cfg) {
   }
   const int64_t tokens = c.cu[c.batch] - c.cu[0];
   TuneKey key{c.d, c.dtype, c.out_dtype, tokens, c.h_q, c.h_q / c.h_kv,
-              c.window > 0 ? c.window : 0, c.batch, c.n_split, c.flags};
+              c.window > 0 ? c.window : 0, c.batch, c.n_split,
+              c.flags | (c.kv_idx ? 0x100 : 0)};  // token-pool calls tune separately
   std::lock_guard<std::mutex> lk(g_tune_mu);
   auto it = g_tune.find(key);
   if (it != g_tune.end()) { *cfg = it->second; return ATTN_OK; }
@@ -296,14 +309,27 @@ int validate(const Call& c) {
       const int64_t sq = (int64_t)c.cu[b + 1] - c.cu[b];
       if (sq < 0) return fail(ATTN_EINVAL, "cu_seqlens_q decreases at %d", b);
       if (c.past[b] < 0) return fail(ATTN_EINVAL, "past_len[%d] < 0", b);
-      if ((int64_t)c.past[b] + sq > c.s_cap)
+      if (c.kv_indptr) {
+        const int64_t n = (int64_t)c.kv_indptr[b + 1] - c.kv_indptr[b];
+        if (c.kv_indptr[b] < 0 || n < 0)
+          return fail(ATTN_EINVAL, "kv_indptr negative or decreasing at %d", b);
+        if ((int64_t)c.past[b] + sq > n)
+          return fail(ATTN_EINVAL, "sequence %d has %lld pool indices for %lld keys", b,
+                      (long long)n, (long long)c.past[b] + sq);
+      } else if ((int64_t)c.past[b] + sq > c.s_cap) {
         return fail(ATTN_EINVAL, "past_len + sq > s_cap for sequence %d", b);
+      }
     }
   }
   const int64_t tokens = c.batch > 0 ? c.cu[c.batch] : 0;
   if (tokens > 0 && (!c.q || !c.k || !c.v || !c.out))
     return fail(ATTN_EINVAL, "null tensor pointer");
   if (c.scale != c.scale || std::isinf(c.scale)) return fail(ATTN_EINVAL, "scale not finite");
+  if (c.kv_indptr || c.kv_idx) {
+    if (c.batch > 0 && !c.kv_indptr) return fail(ATTN_EINVAL, "null kv_indptr");
+    if (tokens > 0 && !c.kv_idx) return fail(ATTN_EINVAL, "null kv_indices");
+    if (c.n_pool < 1) return fail(ATTN_EINVAL, "n_pool < 1");
+  }
   if (c.log) {
     if (c.log->capacity < 0 || (c.log->capacity > 0 && !c.log->records))
       return fail(ATTN_EINVAL, "bad tile log");
@@ -331,6 +357,9 @@ int validate(const Call& c) {
       return fail(ATTN_DECLINED, "tensor pointers must be 16-byte aligned");
     if (c.n_split > 1 && mis(c.workspace))
       return fail(ATTN_DECLINED, "the split workspace must be 16-byte aligned");
+    // pool byte offsets travel as 32-bit load offsets
+    if (c.kv_idx && c.n_pool * c.h_kv * c.d * 2 > (int64_t)0xffffffffu)
+      return fail(ATTN_DECLINED, "token pool above 4 GiB per tensor not supported");
   }
   return ATTN_OK;
 }
@@ -422,6 +451,29 @@ int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
     c.flags = flags;
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
+    return run(c);
+  } catch (...) {
+    return fail(ATTN_EHIP, "internal error");
+  }
+}
+
+int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool, int64_t n_pool,
+                       const int32_t* kv_indices, const int32_t* kv_indptr,
+                       const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
+                       int32_t window, const float* head_sink, float scale, void* out,
+                       float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
+                       int32_t out_dtype, int32_t flags, attn_tile_log* tile_log,
+                       void* stream) {
+  try {
+    Call c{q, k_pool, v_pool, out, head_sink, cu_seqlens_q, past_len, batch, window, h_q,
+           h_kv, d, 0, dtype, out_dtype, scale, tile_log, reinterpret_cast<hipStream_t>(stream)};
+    c.lse = lse;
+    c.flags = flags;
+    c.kv_idx = kv_indices;
+    c.kv_indptr = kv_indptr;
+    c.n_pool = n_pool;
+    // null index arrays would make this a dense call with s_cap 0: name them
+    if (batch > 0 && (!kv_indptr || !kv_indices)) return fail(ATTN_EINVAL, "null kv_indptr / kv_indices");
     return run(c);
   } catch (...) {
     return fail(ATTN_EHIP, "internal error");

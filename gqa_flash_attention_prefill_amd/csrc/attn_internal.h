@@ -17,6 +17,7 @@ struct SeqTable {
   int32_t cu_q[kMaxSeq + 1];      // cumulative chunk lengths (rows of q/out)
   int32_t past[kMaxSeq];          // cached keys before each chunk
   int32_t slot[kMaxSeq];          // cache slot (index into the batch dimension)
+  int32_t kv_start[kMaxSeq];      // token-pool layout: first entry of each sequence in kv_idx
 };
 
 struct Params {
@@ -40,6 +41,11 @@ struct Params {
   int32_t n_split;     // 1: the kernel writes `out`; > 1: it writes partials for attn merge
   int32_t ws_tokens;   // q rows of the whole call (workspace stride)
   int32_t causal;      // 0: non-causal (split/lse kernel variant only)
+  // Token-pool layout (split/lse kernel variant only): k and v are pools
+  // [n_pool, h_kv, d]; key k of sequence b is pool row kv_idx[kv_start[b] + k].
+  const int32_t* kv_idx;  // nullptr: dense caches [batch, h_kv, s_cap, d]
+  uint32_t kv_row_bytes;  // bytes between consecutive pool rows (h_kv * d * 2)
+  uint32_t n_pool;        // pool rows (indices are clamped below it)
   SeqTable seq;
 };
 

@@ -401,7 +401,13 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
     }
   }
 
-  const int64_t kv_base = ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
+  // Token-pool layout (split/lse variant only): key k of this sequence is
+  // pool row kv_list[k], rows h_kv * d elements apart; otherwise the dense
+  // cache of this sequence's slot and KV head.
+  const bool paged = XTRA && p.kv_idx != nullptr;
+  const int32_t* kv_list = paged ? p.kv_idx + p.seq.kv_start[bi] : nullptr;
+  const int64_t kv_base =
+      paged ? (int64_t)g * D : ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
   const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
   const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
 
@@ -434,6 +440,19 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   // instead: every slot a wave reads then holds finite cache data, which
   // matters because a wave without a tile still multiplies P = 0 by V.
   const uint32_t lds_addr = lds_byte_addr(lds);
+  // Token-pool layout: the pool row of each of this lane's keys in the next
+  // stage to load, read one stage ahead so that the index latency hides
+  // behind the stage before it (keys past the sequence read row skv - 1).
+  uint32_t prow[LD_PER_WAVE];
+  auto stage_key = [&](int stage, int i) {
+    const int tt = (wave * LD_PER_WAVE + i) / (TILE_CH / 64);
+    const int t = min(t_lo + stage * S + (tt >> 1), t_hi);
+    return min(t * BKV + ld_key[i], skv - 1);
+  };
+  auto fetch_rows = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < LD_PER_WAVE; ++i) prow[i] = (uint32_t)kv_list[stage_key(stage, i)];
+  };
   auto load_stage = [&](int stage) {
     const uint32_t st = lds_addr + (uint32_t)((stage % NSLOT) * STAGE_CH) * 16u;
 #pragma unroll
@@ -441,6 +460,14 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
       const int qi = wave * LD_PER_WAVE + i;
       const int tt = qi / (TILE_CH / 64);      // tile-tensor: 2 * split + (0 K, 1 V)
       const int blk = qi % (TILE_CH / 64);
+      const uint32_t lds_dst = st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u;
+      if (paged) {
+        // pool row (clamped into the pool) + this lane's chunk of the row
+        const uint32_t r = min(prow[i], p.n_pool - 1u);
+        lds_dma16((tt & 1) ? vptr : kptr,
+                  r * p.kv_row_bytes + ld_off[i] - (uint32_t)ld_key[i] * (D * 2), lds_dst);
+        continue;
+      }
       const int t = min(t_lo + stage * S + (tt >> 1), t_hi);
       const char* tile = reinterpret_cast<const char*>((tt & 1) ? vptr : kptr) +
                          (int64_t)t * (BKV * D * 2);
@@ -450,7 +477,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
         const int row = min(ld_key[i], skv - 1 - t * BKV);
         voff -= (uint32_t)(ld_key[i] - row) * (D * 2);
       }
-      lds_dma16(tile, voff, st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
+      lds_dma16(tile, voff, lds_dst);
     }
   };
   // wait until every stage but the newest one has landed in LDS (`newest`:
@@ -568,13 +595,30 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   int n_visited = 0, t_first = -1, t_last = -1;  // what the loop walks (tile log)
 
   // ---- prologue: stages 0 and 1 resident, S of the wave's first tile ----
-  load_stage(0);
-  if (n_stages > 1) load_stage(1);
-  {
-    const bool newest = NSLOT == 4 && n_stages > 2;
-    if (newest) load_stage(2);
-    wait_older(newest);  // stages 0 and 1 landed
+  if (paged) {
+    // the pool rows of the first stages are read together, then each stage
+    // is issued (one index round trip instead of one per stage)
+    constexpr int PRE = NSLOT - 1;
+    uint32_t pre[PRE][LD_PER_WAVE];
+#pragma unroll
+    for (int s2 = 0; s2 < PRE; ++s2)
+#pragma unroll
+      for (int i = 0; i < LD_PER_WAVE; ++i) pre[s2][i] = (uint32_t)kv_list[stage_key(s2, i)];
+#pragma unroll
+    for (int s2 = 0; s2 < PRE; ++s2) {
+      // the same stages as the dense path: 0 always, 1 and (4-slot ring) 2 if they exist
+      if ((s2 == 1 && n_stages <= 1) || (s2 == 2 && n_stages <= 2)) break;
+#pragma unroll
+      for (int i = 0; i < LD_PER_WAVE; ++i) prow[i] = pre[s2][i];
+      load_stage(s2);
+    }
+    if (NSLOT - 1 < n_stages) fetch_rows(NSLOT - 1);
+  } else {
+    load_stage(0);
+    if (n_stages > 1) load_stage(1);
+    if (NSLOT == 4 && n_stages > 2) load_stage(2);
   }
+  wait_older(NSLOT == 4 && n_stages > 2);  // stages 0 and 1 landed
   __syncthreads();
 
   f32x16 s_a[NB], s_b[NB];   // scores of the current / next tile, roles alternate
@@ -622,6 +666,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kern
   auto stage_step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
     const bool newest = j + NSLOT - 1 < n_stages;
     if (newest) load_stage(j + NSLOT - 1);
+    if (paged && j + NSLOT < n_stages) fetch_rows(j + NSLOT);
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
       const int ts = t_lo + j * S + s2;
@@ -832,7 +877,13 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     }
   }
 
-  const int64_t kv_base = ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
+  // Token-pool layout (split/lse variant only): key k of this sequence is
+  // pool row kv_list[k], rows h_kv * d elements apart; otherwise the dense
+  // cache of this sequence's slot and KV head.
+  const bool paged = XTRA && p.kv_idx != nullptr;
+  const int32_t* kv_list = paged ? p.kv_idx + p.seq.kv_start[bi] : nullptr;
+  const int64_t kv_base =
+      paged ? (int64_t)g * D : ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
   const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
   const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
   u32x4* const ring = lds + grp * GROUP_CH;
@@ -858,6 +909,18 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // A group-local index past the group's last tile loads tile t_hi instead,
   // so every slot a wave reads holds finite cache data (a wave without a
   // tile still multiplies P = 0 by its V fragments).
+  // Token-pool layout: the pool row of each of this lane's keys in the next
+  // tile to load, read one tile ahead so that the index latency hides behind
+  // the phases before it (keys past the sequence read row skv - 1).
+  uint32_t prow[LPW];
+  auto tile_key = [&](int j, int i) {
+    const int t = min(t_lo + 2 * j + grp, t_hi);
+    return min(t * BKV + ld_key[i], skv - 1);
+  };
+  auto fetch_rows = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) prow[i] = (uint32_t)kv_list[tile_key(j, i)];
+  };
   auto load_tile = [&](int j) {
     const int t = min(t_lo + 2 * j + grp, t_hi);
     const uint32_t st = ring_addr + (uint32_t)((j % NS) * SLOT_CH) * 16u;
@@ -867,6 +930,13 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       const int qi = rg * LPW + i;
       const int tt = qi / (TILE_CH / 64);
       const int blk = qi % (TILE_CH / 64);
+      if (paged) {
+        // pool row (clamped into the pool) + this lane's chunk of the row
+        const uint32_t r = min(prow[i], p.n_pool - 1u);
+        lds_dma16(tt ? vptr : kptr, r * p.kv_row_bytes + ld_off[i] - (uint32_t)ld_key[i] * (D * 2),
+                  st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
+        continue;
+      }
       const char* tile = reinterpret_cast<const char*>(tt ? vptr : kptr) + (int64_t)t * (BKV * D * 2);
       uint32_t voff = ld_off[i];
       if (tail) {
@@ -1091,9 +1161,27 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   };
 
   // ---- prologue: tiles 0 .. NS-2 requested, 0 and 1 landed ----
+  if (paged) {
+    // the pool rows of the first tiles are read together, then each tile is
+    // issued (one index round trip instead of one per tile)
+    uint32_t pre[NS - 1][LPW];
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < n_stages) load_tile(j);
+    for (int j = 0; j < NS - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) pre[j][i] = (uint32_t)kv_list[tile_key(j, i)];
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+      if (j >= n_stages) break;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) prow[i] = pre[j][i];
+      load_tile(j);
+    }
+    if (NS - 1 < n_stages) fetch_rows(NS - 1);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < n_stages) load_tile(j);
+  }
   {
     const int newest = min(NS - 2, n_stages - 1);
     if (newest - 1 >= 2 && NS == 5)
@@ -1114,6 +1202,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     // the direct loads go after the MFMAs: issued while the last ones drain
     __builtin_amdgcn_sched_barrier(0);
     if (j >= 0 && j + NS - 1 < n_stages) load_tile(j + NS - 1);
+    if (paged && j >= 0 && j + NS < n_stages) fetch_rows(j + NS);
     __builtin_amdgcn_s_setprio(0);
     barrier();
     // ---- V_j ----
@@ -1188,7 +1277,7 @@ void launch_pp_x(const Params& p, int n_items, hipStream_t stream) {
 
 template <int D, int BKV, int NS, typename TI, typename TO>
 hipError_t launch_pp(const Params& p, int n_items, hipStream_t stream) {
-  if (p.n_split > 1 || p.lse != nullptr || !p.causal)
+  if (p.n_split > 1 || p.lse != nullptr || !p.causal || p.kv_idx != nullptr)
     launch_pp_x<D, BKV, NS, true, TI, TO>(p, n_items, stream);
   else
     launch_pp_x<D, BKV, NS, false, TI, TO>(p, n_items, stream);
@@ -1209,7 +1298,7 @@ void launch_x(const Params& p, int n_items, hipStream_t stream) {
 
 template <int D, int BKV, int R, int S, int NS, typename TI, typename TO>
 hipError_t launch(const Params& p, int n_items, hipStream_t stream) {
-  if (p.n_split > 1 || p.lse != nullptr || !p.causal)
+  if (p.n_split > 1 || p.lse != nullptr || !p.causal || p.kv_idx != nullptr)
     launch_x<D, BKV, R, S, NS, true, TI, TO>(p, n_items, stream);
   else
     launch_x<D, BKV, R, S, NS, false, TI, TO>(p, n_items, stream);

@@ -65,7 +65,7 @@ extern "C" {
 
 enum { ATTN_OK = 0, ATTN_DECLINED = -1, ATTN_EINVAL = -2, ATTN_EHIP = -3 };
 enum { ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_F32 = 3 };
-enum { ATTN_FLAG_NONCAUSAL = 1 };  /* attn_prefill_split flags */
+enum { ATTN_FLAG_NONCAUSAL = 1 };  /* attn_prefill_split / attn_prefill_paged flags */
 
 /* Fields of one visited-tile record (int32 each). */
 enum {
@@ -168,6 +168,41 @@ int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
                        float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t s_cap,
                        int32_t dtype, int32_t out_dtype, int32_t n_split, int32_t flags,
                        void* workspace, int64_t workspace_bytes, attn_tile_log* tile_log,
+                       void* stream);
+
+/*
+ * Ragged batch over a token-pool KV layout (sglang pull request 34468,
+ * "Commit 1": the extend kernel reads the cached prefix through kv_indptr /
+ * kv_indices into a pool of token slots, and its window-bounded variant
+ * through window_kv_indptr / window_kv_indices).  Key k of sequence b -- the
+ * cached prefix and the chunk's own keys alike, k < past_len[b] + sq_b -- is
+ * pool row kv_indices[kv_indptr[b] + k].  A window-bounded list is the same
+ * call with past_len[b] = the number of prefix keys the list keeps: both mask
+ * bounds compare a key with its own row's position, so dropping prefix keys
+ * no row keeps and shifting positions changes nothing.
+ *   q, out       as attn_prefill_varlen ([tokens, h_q, d])
+ *   k_pool, v_pool  DEVICE [n_pool, h_kv, d] (q dtype), 16-byte aligned; the
+ *                caller has written the chunk's own keys / values into the
+ *                rows its list names.  n_pool * h_kv * d * 2 must be at most
+ *                4 GiB - 1 (else -1: pool offsets travel as 32-bit offsets).
+ *   kv_indices   DEVICE int32: pool rows.  An entry outside [0, n_pool) is
+ *                clamped into the pool (the read stays in bounds; the result
+ *                for that key is then another row's).
+ *   kv_indptr    HOST int32 [batch + 1], non-decreasing, kv_indptr[0] >= 0;
+ *                sequence b needs kv_indptr[b + 1] - kv_indptr[b] >=
+ *                past_len[b] + sq_b (extra entries are never read).
+ *   lse, flags   as attn_prefill_split (NULL / 0 for none); no KV splits.
+ * The kernels, their tile floor / ceiling and the tile log are those of the
+ * dense call; only the address of each key row differs.  Errors as
+ * attn_prefill_varlen, with the cache-length check replaced by the index-list
+ * length check; -2 also for null kv_indptr / kv_indices or n_pool < 1.
+ */
+int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool, int64_t n_pool,
+                       const int32_t* kv_indices, const int32_t* kv_indptr,
+                       const int32_t* cu_seqlens_q, const int32_t* past_len, int32_t batch,
+                       int32_t window, const float* head_sink, float scale, void* out,
+                       float* lse, int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
+                       int32_t out_dtype, int32_t flags, attn_tile_log* tile_log,
                        void* stream);
 
 /* Bytes of workspace attn_prefill_split needs (0 for n_split = 1; -1 for

@@ -140,3 +140,27 @@ def test_split_entry_validates_before_any_gpu_call():
     assert call(4, ctypes.c_void_p(0x10004), need) == binding.ATTN_DECLINED
     assert call(1, None, 0, flags=2) == binding.ATTN_EINVAL
     assert "flags" in binding.attn_last_error()
+
+
+def test_paged_entry_validates_before_any_gpu_call():
+    L = binding.lib()
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+    def call(indptr, past, sq=64, n_pool=4096, idx=fake, h_kv=2, d=64, ptr=fake):
+        cu = (ctypes.c_int32 * 2)(0, sq)
+        ip = None if indptr is None else (ctypes.c_int32 * len(indptr))(*indptr)
+        pl = (ctypes.c_int32 * 1)(past)
+        return L.attn_prefill_paged(ptr, ptr, ptr, n_pool, idx, ip, cu, pl, 1, -1, None,
+                                    ctypes.c_float(0.125), ptr, None, 8, h_kv, d,
+                                    binding.ATTN_F16, binding.ATTN_F16, 0, None, None)
+
+    assert call(None, 0) == binding.ATTN_EINVAL                 # no kv_indptr
+    assert call([0, 100], 0, idx=None) == binding.ATTN_EINVAL   # no kv_indices
+    assert call([0, 100], 50) == binding.ATTN_EINVAL            # 100 indices for 114 keys
+    assert "pool indices" in binding.attn_last_error()
+    assert call([5, 3], 0) == binding.ATTN_EINVAL               # decreasing kv_indptr
+    assert call([-1, 200], 0) == binding.ATTN_EINVAL            # negative start
+    assert call([0, 100], 0, n_pool=0) == binding.ATTN_EINVAL
+    # pool offsets are 32-bit: 2^23 rows x 2 heads x 128 x 2 bytes = 4 GiB declines
+    assert call([0, 100], 0, n_pool=1 << 23, d=128) == binding.ATTN_DECLINED
+    assert call([0, 100], 0, ptr=ctypes.c_void_p(0x10008)) == binding.ATTN_DECLINED
