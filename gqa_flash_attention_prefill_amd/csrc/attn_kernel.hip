@@ -960,7 +960,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   f32x16 negm1 = f32x16{};
   // Row sums of P on the matrix pipe: ones . P^T puts the sum of P over the
   // tile's keys in every element of the row's column (the vector pipe is the
-  // busier one at d = 64).
+  // busier one at d = 64).  fp16 inputs: the tile's four 16-key P vectors are
+  // first added as packed fp16 (p <= 2^8, so a sum of four stays below
+  // 2^10; one rounding of 2^-11 relative per add), then one MFMA sums them;
+  // bf16 inputs: one MFMA per 16-key step for each of P's two parts.
   f32x16 lsum = f32x16{};
   const u32x4 ones = {TI::kOnePair, TI::kOnePair, TI::kOnePair, TI::kOnePair};
   f32x16 acc[DB];
@@ -1031,8 +1034,17 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         if (g16 == 0 && db == 0) refill_k(NB * KSTEPS - 1);
         else if (db > 0) vf[db - 1][g16] = v_frag<D>(vt, g16, db - 1, lane);
       }
-      lsum = TI::mma(ones, pb[g16], lsum);
-      if constexpr (TI::kSplitP) lsum = TI::mma(ones, pl[g16], lsum);
+      if constexpr (TI::kSplitP) {
+        lsum = TI::mma(ones, pb[g16], lsum);
+        lsum = TI::mma(ones, pl[g16], lsum);
+      } else if (g16 == NG - 1) {
+        // fp16 P of the tile's 16-key steps added as whole vectors (packed
+        // fp16 adds), then one row-sum MFMA for the tile
+        f16x8 sum = __builtin_bit_cast(f16x8, pb[0]);
+#pragma unroll
+        for (int g2 = 1; g2 < NG; ++g2) sum += __builtin_bit_cast(f16x8, pb[g2]);
+        lsum = TI::mma(ones, __builtin_bit_cast(u32x4, sum), lsum);
+      }
       vf[DB - 1][g16] = v_frag<D>(vt, g16, DB - 1, lane);
     }
     // issue order as written: each read follows the MFMA after the one that
@@ -1051,7 +1063,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         if (g16 == 0 && db == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
         else if (db > 0) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kMfma, PVM, 0);
+      if (TI::kSplitP || g16 == NG - 1) __builtin_amdgcn_sched_group_barrier(kMfma, PVM, 0);
       __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
     }
   };
