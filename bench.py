@@ -421,6 +421,70 @@ def paged_demo(torch, binding):
                         "H_q 64 / H_kv 8, d 64, fp16, sinks, full attention", "results": res}
 
 
+def configs_demo(torch, binding):
+    """The other workloads of this path, each timed as one call (the tuning
+    sweep first, then the mean of 50 back-to-back calls between one event
+    pair): the tiny case, a gpt-oss-20b full-attention layer (4096 rows, no
+    prefix), the window-128 chunk of 512 rows at past 0 / 512 / 8192 (full
+    prefix in the cache), and the ragged bf16 d 128 batch of 8 sequences with
+    fp32 and bf16 outputs.  Useful TFLOP/s counts kept pairs only; GB/s is
+    algorithmic bytes (q + out + each sequence's kept-key union of K and V,
+    read once) per call time."""
+    from gqa_flash_attention_prefill_amd import synth
+    L = binding.lib()
+    cases = [(synth.tiny(), None), (synth.full_sq4096(), None), (synth.swa_chunk(0), None),
+             (synth.swa_chunk(512), None), (synth.swa_chunk(8192), None),
+             (synth.ragged_bf16(), torch.float32), (synth.ragged_bf16(), None)]
+    res = []
+    for case, out_dtype in cases:
+        c2 = synth.Case(case.name, h_q=case.h_q, h_kv=case.h_kv, d=case.d, sq=list(case.sq),
+                        past=list(case.past), window=case.window, dtype=case.dtype,
+                        seed=case.seed, poison_tail=False)
+        inp = synth.make(c2, device="cuda")
+        q = inp["q"]
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device="cuda")
+        cu, past, w = inp["cu_seqlens"], inp["past_len"], inp["window"]
+        batch, h_kv, s_cap, d = inp["k_cache"].shape
+        code = {torch.float16: binding.ATTN_F16, torch.bfloat16: binding.ATTN_BF16,
+                torch.float32: binding.ATTN_F32}
+        args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(inp["k_cache"].data_ptr()),
+                ctypes.c_void_p(inp["v_cache"].data_ptr()),
+                (ctypes.c_int32 * len(cu))(*cu), (ctypes.c_int32 * len(past))(*past), len(past),
+                w, ctypes.c_void_p(inp["sink"].data_ptr()), ctypes.c_float(c2.scale),
+                ctypes.c_void_p(out.data_ptr()), c2.h_q, h_kv, d, s_cap, code[q.dtype],
+                code[out.dtype], None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        for _ in range(3):
+            if L.attn_prefill_varlen(*args) != 0:
+                raise RuntimeError(binding.attn_last_error())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            L.attn_prefill_varlen(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 50
+        pairs, keys = 0, 0
+        for b in range(len(past)):
+            sq = cu[b + 1] - cu[b]
+            pos = past[b] + np.arange(sq, dtype=np.int64)
+            lo = np.zeros_like(pos) if w <= 0 else np.maximum(0, pos - w + 1)
+            pairs += int((pos - lo + 1).sum())
+            keys += past[b] + sq - (0 if w <= 0 else max(0, past[b] - w + 1))
+        fl = 4.0 * d * c2.h_q * pairs
+        tokens = cu[-1]
+        nbytes = (tokens * c2.h_q * d * (q.element_size() + out.element_size())
+                  + 2 * keys * h_kv * d * q.element_size())
+        idx = binding.attn_tuned_config(d, q.dtype, out.dtype, tokens, c2.h_q, h_kv, w, len(past))
+        res.append({"workload": case.name + ("" if out_dtype is None else "_fp32out"),
+                    "us": round(us, 2), "useful_tflops": round(fl / us / 1e6, 2),
+                    "frac_peak": round(fl / us / 1e6 / PEAK_TFLOPS_F16, 4),
+                    "algorithmic_gbs": round(nbytes / us / 1e3, 1),
+                    "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                    "config": binding.attn_config_name(idx) if idx >= 0 else None})
+    return {"workload": "the other workloads of this path, one call each", "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -433,6 +497,9 @@ def main():
                     help="time KV splits on a few-Q-tile call (prints its own JSON line)")
     ap.add_argument("--paged-demo", action="store_true",
                     help="time the token-pool layout against dense caches (prints its own JSON line)")
+    ap.add_argument("--configs-demo", action="store_true",
+                    help="time the tiny, 4096-row, window-chunk and ragged bf16 workloads "
+                         "(prints its own JSON line)")
     ap.add_argument("--detail", default=None, help="write per-chunk timings (JSON) here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run the 1 GiB cold copy used to scale HBM counters")
@@ -467,9 +534,10 @@ def main():
     if args.one_call is not None:
         one_call(torch, binding, args.one_call)
         return
-    if args.split_demo or args.decode_demo or args.paged_demo:
+    if args.split_demo or args.decode_demo or args.paged_demo or args.configs_demo:
         torch.cuda.set_device(0)
-        demo = split_demo if args.split_demo else (decode_demo if args.decode_demo else paged_demo)
+        demo = (split_demo if args.split_demo else decode_demo if args.decode_demo
+                else paged_demo if args.paged_demo else configs_demo)
         print(json.dumps(demo(torch, binding)), flush=True)
         return
     dev = "cuda:0"
