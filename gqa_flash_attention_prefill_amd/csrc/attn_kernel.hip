@@ -298,7 +298,12 @@ __device__ inline void split_range(const Params& p, int* t_lo, int* t_hi) {
 // so matrix and vector work of neighbouring tiles overlap inside the wave.
 template <int D, int BKV, int R, int S_REQ, int NSLOT, bool WIN, bool XTRA, typename TI,
           typename TO>
-__global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64) void attn_fwd_kernel(Params p) {
+// At least two waves per SIMD for d <= 128 (registers capped at 256 per
+// wave): the small-tile configurations serve latency-bound calls (window
+// chunks, decode rows, short ragged sequences), where a second resident wave
+// hides more of each load than the registers it gives up would buy.  At
+// d = 256 the accumulators alone need one wave per SIMD.
+__global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)) void attn_fwd_kernel(Params p) {
   // stages of two 64-key d=128 tiles would not fit in LDS: d >= 128 uses one
   // split (and d = 256 32-key tiles, chosen by its launcher)
   constexpr int S = (D >= 128) ? 1 : S_REQ;
