@@ -12,16 +12,18 @@
 // head of the group ("no-expand" GQA: KV heads are never replicated).
 //
 // Per KV tile (BKV keys):
-//   * K and V are read from HBM with 16-byte coalesced loads into registers
-//     one stage ahead, then stored to a double-buffered LDS stage (both
-//     row-major, XOR-swizzled in 16-byte chunks); one barrier per stage;
+//   * K and V move from HBM straight into an LDS ring (global_load_lds
+//     direct loads, 16 bytes per lane, both row-major and XOR-swizzled in
+//     16-byte chunks) several tiles ahead of their use; a barrier per stage
+//     hands a landed tile to every wave;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_{f16,bf16}: with K as the A operand
 //     and the wave's Q (held in registers for the whole loop) as B, each
 //     lane's accumulator holds ONE query row (lane % 32) and 16 keys, so the
 //     row max is an in-lane reduction plus one exchange with lane ^ 32 and
 //     the rescale of the output accumulator is lane-local;
-//   * mask only on boundary tiles; online softmax in exp2 space (scores are
-//     scaled by scale * log2 e inside the exponent's FMA); the reference max
+//   * mask only on boundary tiles; online softmax in exp2 space (fp16 Q is
+//     pre-scaled by scale * log2 e and the running max enters as the MFMA's
+//     accumulator input; bf16 applies both in one FMA); the reference max
 //     is raised lazily (only when a row's tile max exceeds it by 2^8), which
 //     skips most accumulator rescales; a row that has seen no key and whose
 //     tile is fully masked keeps m = -inf and is guarded ("window in v5":
@@ -34,7 +36,11 @@
 //     costs ~1e-3 relative error.
 //   * Two waves per row group (KV splits) take alternate tiles, so each
 //     SIMD holds two independent waves; their partial (m, l, O) are merged
-//     through LDS before the epilogue.
+//     through LDS before the epilogue.  Two kernels share all of the above:
+//     attn_fwd_kernel, where each wave software-pipelines the matrix work of
+//     one tile with the vector work of the previous one, and attn_pp_kernel
+//     (d 64), where the two waves of a SIMD alternate whole matrix and
+//     vector phases between workgroup barriers.
 //
 // KV loop bounds ("window in v5"; sglang 34468 "bound the stage-1 prefix
 // loop"): the loop starts at the tile holding the lowest key the Q tile's
@@ -285,9 +291,9 @@ __device__ inline void split_range(const Params& p, int* t_lo, int* t_hi) {
 // 32 Q-tile rows; split sp takes every S-th KV tile of the workgroup's range,
 // so the S waves of a row group (two per SIMD) work on different tiles at
 // once and are merged through LDS at the end.  K/V of the S tiles of one
-// stage sit in one LDS slot of a 3-slot ring: while stage j is consumed,
-// stage j + 1 is resident and stage j + 2 is loaded (global -> registers ->
-// LDS), with one barrier per stage.
+// stage sit in one LDS slot of a 3- or 4-slot ring: while stage j is
+// consumed, stage j + 1 is resident and stage j + 2 (and j + 3) is loaded by
+// direct global -> LDS loads, with one barrier per stage.
 //
 // Each wave runs its tiles as a two-phase software pipeline:
 //   phase A  MFMA: S_{i+1} = K_{i+1} . Q^T      VALU: P_i = exp2(S_i), 16-bit
@@ -321,7 +327,13 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   static_assert(BKV % 32 == 0 && (D == 64 || D == 128 || D == 256), "tile shape");
   static_assert(S == 1 || S == 2, "1 or 2 KV splits");
 
-  __shared__ u32x4 lds[NSLOT * STAGE_CH];
+  // Separate K and V rings of KD = NSLOT - 1 slots (S tiles each): the K of
+  // stage s is read one step before its V (as the next tile's scores), so
+  // each tensor is loaded exactly one step before its first reader and
+  // neither ring needs a third slot.
+  constexpr int KD = NSLOT - 1;
+  constexpr int RING_CH = KD * S * TILE_CH;  // one tensor's ring
+  __shared__ u32x4 lds[2 * RING_CH];         // K ring, then V ring
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -426,6 +438,9 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   // skv - 1 (finite data whose scores the causal mask removes, p = 0).
   constexpr int LD_PER_WAVE = STAGE_CH / 64 / NW;
   static_assert(STAGE_CH % (64 * NW) == 0 && TILE_CH % 64 == 0, "direct loads tile the stage");
+  // with a 4-slot ring the waits let one step's loads stay in flight, which
+  // needs every wave's loads of a step to be of one tensor (K or V)
+  static_assert(NSLOT == 3 || (TILE_CH / 64) % LD_PER_WAVE == 0, "one tensor per wave");
   // this lane's key and byte offset inside its tile for each of the wave's
   // loads (the same every stage)
   int ld_key[LD_PER_WAVE];
@@ -445,27 +460,35 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   // instead: every slot a wave reads then holds finite cache data, which
   // matters because a wave without a tile still multiplies P = 0 by V.
   const uint32_t lds_addr = lds_byte_addr(lds);
+  // Each step loads this wave's pieces of a stage's K / V tile-tensors:
+  // K pieces of stage kst, V pieces of stage vst (a negative stage: none).
+  auto piece_is_v = [&](int i) { return (((wave * LD_PER_WAVE + i) / (TILE_CH / 64)) & 1) != 0; };
+  auto piece_stage = [&](int i, int kst, int vst) { return piece_is_v(i) ? vst : kst; };
   // Token-pool layout: the pool row of each of this lane's keys in the next
-  // stage to load, read one stage ahead so that the index latency hides
-  // behind the stage before it (keys past the sequence read row skv - 1).
+  // loads, read one step ahead so that the index latency hides behind the
+  // step before it (keys past the sequence read row skv - 1).
   uint32_t prow[LD_PER_WAVE];
-  auto stage_key = [&](int stage, int i) {
+  auto piece_key = [&](int i, int stage) {
     const int tt = (wave * LD_PER_WAVE + i) / (TILE_CH / 64);
-    const int t = min(t_lo + stage * S + (tt >> 1), t_hi);
+    const int t = min(t_lo + max(stage, 0) * S + (tt >> 1), t_hi);
     return min(t * BKV + ld_key[i], skv - 1);
   };
-  auto fetch_rows = [&](int stage) {
+  auto fetch_rows = [&](int kst, int vst) {
 #pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) prow[i] = (uint32_t)kv_list[stage_key(stage, i)];
+    for (int i = 0; i < LD_PER_WAVE; ++i)
+      prow[i] = (uint32_t)kv_list[piece_key(i, piece_stage(i, kst, vst))];
   };
-  auto load_stage = [&](int stage) {
-    const uint32_t st = lds_addr + (uint32_t)((stage % NSLOT) * STAGE_CH) * 16u;
+  auto load_kv = [&](int kst, int vst) {
 #pragma unroll
     for (int i = 0; i < LD_PER_WAVE; ++i) {
       const int qi = wave * LD_PER_WAVE + i;
       const int tt = qi / (TILE_CH / 64);      // tile-tensor: 2 * split + (0 K, 1 V)
       const int blk = qi % (TILE_CH / 64);
-      const uint32_t lds_dst = st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u;
+      const int stage = (tt & 1) ? vst : kst;
+      if (stage < 0) continue;
+      const uint32_t lds_dst =
+          lds_addr + (uint32_t)((tt & 1) * RING_CH + (stage % KD) * S * TILE_CH +
+                                (tt >> 1) * TILE_CH + blk * 64) * 16u;
       if (paged) {
         // pool row (clamped into the pool) + this lane's chunk of the row
         const uint32_t r = min(prow[i], p.n_pool - 1u);
@@ -485,8 +508,11 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
       lds_dma16(tile, voff, lds_dst);
     }
   };
-  // wait until every stage but the newest one has landed in LDS (`newest`:
-  // whether a newer stage's loads were issued after it)
+  // does this wave issue any piece for (kst, vst)?  (its pieces are of one
+  // tensor whenever the answer decides a wait)
+  auto issues = [&](int kst, int vst) { return piece_is_v(0) ? vst >= 0 : kst >= 0; };
+  // wait until every load but this step's newest ones has landed in LDS
+  // (`newest`: whether this wave issued loads in this step)
   auto wait_older = [&](bool newest) {
     if (NSLOT == 4 && newest)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(LD_PER_WAVE));
@@ -599,37 +625,38 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
 
   int n_visited = 0, t_first = -1, t_last = -1;  // what the loop walks (tile log)
 
-  // ---- prologue: stages 0 and 1 resident, S of the wave's first tile ----
+  // ---- prologue: K of stages 0 .. KD-1 and V of stages 0 .. KD-2 (the
+  // first K and V always, later ones if the stage exists); then every one
+  // but the last step's is resident, and S of the wave's first tile ----
+  auto pro_k = [&](int s2) { return (s2 == 0 || s2 < n_stages) ? s2 : -1; };
+  auto pro_v = [&](int s2) { return (s2 == 1 || (s2 >= 1 && s2 - 1 < n_stages)) ? s2 - 1 : -1; };
   if (paged) {
-    // the pool rows of the first stages are read together, then each stage
-    // is issued (one index round trip instead of one per stage)
-    constexpr int PRE = NSLOT - 1;
-    uint32_t pre[PRE][LD_PER_WAVE];
+    // the pool rows of the first steps are read together, then each step's
+    // loads are issued (one index round trip instead of one per step)
+    uint32_t pre[KD][LD_PER_WAVE];
 #pragma unroll
-    for (int s2 = 0; s2 < PRE; ++s2)
+    for (int s2 = 0; s2 < KD; ++s2)
 #pragma unroll
-      for (int i = 0; i < LD_PER_WAVE; ++i) pre[s2][i] = (uint32_t)kv_list[stage_key(s2, i)];
+      for (int i = 0; i < LD_PER_WAVE; ++i)
+        pre[s2][i] = (uint32_t)kv_list[piece_key(i, piece_stage(i, pro_k(s2), pro_v(s2)))];
 #pragma unroll
-    for (int s2 = 0; s2 < PRE; ++s2) {
-      // the same stages as the dense path: 0 always, 1 and (4-slot ring) 2 if they exist
-      if ((s2 == 1 && n_stages <= 1) || (s2 == 2 && n_stages <= 2)) break;
+    for (int s2 = 0; s2 < KD; ++s2) {
 #pragma unroll
       for (int i = 0; i < LD_PER_WAVE; ++i) prow[i] = pre[s2][i];
-      load_stage(s2);
+      load_kv(pro_k(s2), pro_v(s2));
     }
-    if (NSLOT - 1 < n_stages) fetch_rows(NSLOT - 1);
+    fetch_rows(KD < n_stages ? KD : -1, KD - 1 < n_stages ? KD - 1 : -1);
   } else {
-    load_stage(0);
-    if (n_stages > 1) load_stage(1);
-    if (NSLOT == 4 && n_stages > 2) load_stage(2);
+#pragma unroll
+    for (int s2 = 0; s2 < KD; ++s2) load_kv(pro_k(s2), pro_v(s2));
   }
-  wait_older(NSLOT == 4 && n_stages > 2);  // stages 0 and 1 landed
+  wait_older(issues(pro_k(KD - 1), pro_v(KD - 1)));
   __syncthreads();
 
   f32x16 s_a[NB], s_b[NB];   // scores of the current / next tile, roles alternate
   int t_cur = 0;
   if (wave_tile(0, &t_cur)) {
-    scores(lds + (2 * sp) * TILE_CH, t_cur, s_a);
+    scores(lds + sp * TILE_CH, t_cur, s_a);
     const float mx = prepare(t_cur, s_a);
     rebase(mx, s_a);
   } else {
@@ -669,9 +696,14 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   };
 
   auto stage_step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
-    const bool newest = j + NSLOT - 1 < n_stages;
-    if (newest) load_stage(j + NSLOT - 1);
-    if (paged && j + NSLOT < n_stages) fetch_rows(j + NSLOT);
+    // K of stage j + KD (first read by step j + KD - 1) and V of stage
+    // j + KD - 1 (read by that same step); their slots' last readers were
+    // steps j - 1 (K) and j - 1 (V)
+    const int kst = j + KD < n_stages ? j + KD : -1;
+    const int vst = j + KD - 1 < n_stages ? j + KD - 1 : -1;
+    const bool newest = issues(kst, vst);
+    load_kv(kst, vst);
+    if (paged) fetch_rows(j + 1 + KD < n_stages ? j + 1 + KD : -1, j + KD < n_stages ? j + KD : -1);
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
       const int ts = t_lo + j * S + s2;
@@ -684,9 +716,8 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
 
     int t_nxt = 0;
     const bool nxt_ok = wave_tile(j + 1, &t_nxt);
-    const u32x4* k_cur_slot = lds + (j % NSLOT) * STAGE_CH + (2 * sp) * TILE_CH;
-    const u32x4* k_nxt_slot = lds + ((j + 1) % NSLOT) * STAGE_CH + (2 * sp) * TILE_CH;
-    const u32x4* vt = k_cur_slot + TILE_CH;
+    const u32x4* k_nxt_slot = lds + ((j + 1) % KD) * S * TILE_CH + sp * TILE_CH;
+    const u32x4* vt = lds + RING_CH + (j % KD) * S * TILE_CH + sp * TILE_CH;
     // One straight-line body for every stage (no branch on whether this wave
     // has a current or a next tile), so that the scheduler can interleave
     //   S_{i+1} (MFMA) || P_i (VALU);  PV_i (MFMA) || max of S_{i+1} (VALU)
@@ -712,7 +743,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
       set_neg_inf(s_nxt);
     }
 
-    wait_older(newest);  // stage j + 2 landed in LDS
+    wait_older(newest);  // K of stage j + 2 and V of stage j + 1 landed in LDS
     __syncthreads();
   };
 
@@ -724,6 +755,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   // ---- merge the KV splits of each row group through LDS ----
   if constexpr (S > 1) {
     constexpr int NV = 2 + 16 * DB;
+    static_assert(R * NV * 64 * 4 <= 2 * RING_CH * 16, "the merge fits the rings' LDS");
     float* mb = reinterpret_cast<float*>(lds);
     if (sp == 1) {
       float* dst = mb + rg * NV * 64 + lane;
