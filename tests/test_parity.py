@@ -20,22 +20,26 @@ def _gpu():
     yield
 
 
-def _full_check(case, out_dtypes=("same", "f32"), log=True):
+def _full_check(case, out_dtypes=("same", "f32"), log=True, every_config=False):
+    """Whole output against the oracle (and the tile log against the floor
+    formula); with every_config, once per kernel configuration, forced."""
     inp = synth.make(case)
     dev = to_device(inp)
     ref = oracle_full(inp)
-    for od in out_dtypes:
-        tdt = case.torch_dtype if od == "same" else torch.float32
-        cap = case.tokens * case.h_q if log else 0
-        out, recs, bkv, q_rows = run_gpu(dev, out_dtype=tdt, log_capacity=cap)
-        got = f64(out)
-        assert np.all(np.isfinite(got)), f"{case.name}: non-finite output"
-        expect = ref if tdt == torch.float32 else rne(ref, tdt)
-        err = rel_l2(got, expect)
-        print(f"{case.name} out={od}: relL2 {err:.3e}")
-        assert err <= TOL, (case.name, od, err)
-        if log:
-            check_tile_log(recs, bkv, q_rows, case.cu_seqlens, case.past, case.window, case.h_q)
+    for cfg in (_each_config() if every_config else [None]):
+        name = case.name if cfg is None else f"{case.name}[{binding.attn_config_name(cfg)}]"
+        for od in out_dtypes:
+            tdt = case.torch_dtype if od == "same" else torch.float32
+            cap = case.tokens * case.h_q if log else 0
+            out, recs, bkv, q_rows = run_gpu(dev, out_dtype=tdt, log_capacity=cap)
+            got = f64(out)
+            assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+            expect = ref if tdt == torch.float32 else rne(ref, tdt)
+            err = rel_l2(got, expect)
+            print(f"{name} out={od}: relL2 {err:.3e}")
+            assert err <= TOL, (name, od, err)
+            if log:
+                check_tile_log(recs, bkv, q_rows, case.cu_seqlens, case.past, case.window, case.h_q)
     return ref
 
 
@@ -71,7 +75,7 @@ def test_mid_cases(spec):
     case = synth.Case(name, h_q=h_q, h_kv=h_kv, d=d, sq=sq, past=past, window=window,
                       dtype=dtype, sink=sink, seed=77 + sum(sq) + sum(past),
                       s_cap=max(p + s for p, s in zip(past, sq)) + 23)
-    _full_check(case)
+    _full_check(case, every_config=True)
 
 
 def _each_config():
