@@ -428,10 +428,11 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
   const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
 
-  // ---- direct global -> LDS load of one stage ----
-  // The stage is 2S tile-tensors ((split, K|V)) of TILE_CH 16-byte chunks,
-  // moved as 1-KB global_load_lds_dwordx4 loads (lane i's 16 bytes land at
-  // the load's LDS base + 16 i); wave w issues loads w * LD_PER_WAVE + i.
+  // ---- direct global -> LDS loads, one step's worth per call ----
+  // A step moves 2S tile-tensors ((split, K|V)) of TILE_CH 16-byte chunks --
+  // the K tiles of one stage and the V tiles of the stage before it -- as
+  // 1-KB global_load_lds_dwordx4 loads (lane i's 16 bytes land at the load's
+  // LDS base + 16 i); wave w issues loads w * LD_PER_WAVE + i.
   // Lane l of a load fills chunk 64 * block + l of its tile-tensor: key
   // (64 * block + l) / DCH, physical chunk l % DCH, so it fetches logical
   // chunk physical ^ swizzle(key).  Rows at or past skv are read from row
