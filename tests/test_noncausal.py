@@ -71,14 +71,22 @@ def test_noncausal_differs_from_causal():
     case = CASES[0]
     inp = synth.make(case)
     dev = to_device(inp)
-    outs = []
-    for causal in (True, False):
-        out = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
-        binding.attn_prefill_split(dev["q"], dev["k_cache"], dev["v_cache"], dev["cu_seqlens"],
-                                   dev["past_len"], -1, dev["sink"], case.scale, out,
-                                   causal=causal)
-        outs.append(out)
-    torch.cuda.synchronize()
-    # the last row of the chunk sees every key either way; earlier rows do not
-    assert torch.allclose(outs[0][-1], outs[1][-1], atol=1e-6)
-    assert not torch.allclose(outs[0][0], outs[1][0], atol=1e-3)
+    for cfg in _each_config():
+        name = binding.attn_config_name(cfg)
+        outs = []
+        for causal in (True, False):
+            out = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
+            binding.attn_prefill_split(dev["q"], dev["k_cache"], dev["v_cache"],
+                                       dev["cu_seqlens"], dev["past_len"], -1, dev["sink"],
+                                       case.scale, out, causal=causal)
+            outs.append(out)
+        torch.cuda.synchronize()
+        # The last row of the chunk keeps every key either way; the first row
+        # keeps its causal prefix only.  The last row agrees to the parity
+        # bound, not bit for bit: the lazy rescale shares one reference-max
+        # decision among a wave's rows, whose kept keys differ between the
+        # modes, so that row's fp16 P is rounded against different maxima.
+        last = rel_l2(f64(outs[0][-1]), f64(outs[1][-1]))
+        first = rel_l2(f64(outs[0][0]), f64(outs[1][0]))
+        assert last <= TOL, (name, last)
+        assert first > 0.1, (name, first)
