@@ -181,6 +181,7 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
       st.slot[i] = b0 + i;
       st.kv_start[i] = c.kv_indptr ? c.kv_indptr[b0 + i] : 0;
     }
+    st.n_tiles = st.cu_tiles[nb];
     const int64_t n_items = (int64_t)st.cu_tiles[nb] * c.h_kv * p.n_hgroups;
     if (n_items == 0) continue;
     if (n_items > 0x7fffffff) return fail(ATTN_EINVAL, "too many work items (%lld)",

@@ -13,6 +13,7 @@ constexpr int kMaxSeq = 128;
 
 struct SeqTable {
   int32_t n_seq;
+  int32_t n_tiles;                // cu_tiles[n_seq], also read without indexing
   int32_t cu_tiles[kMaxSeq + 1];  // cumulative Q-tile counts
   int32_t cu_q[kMaxSeq + 1];      // cumulative chunk lengths (rows of q/out)
   int32_t past[kMaxSeq];          // cached keys before each chunk

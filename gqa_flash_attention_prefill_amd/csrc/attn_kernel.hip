@@ -221,10 +221,102 @@ __device__ inline uint32_t lds_byte_addr(const void* p) {
 constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | (15 << 8) | (7 << 4) | (n & 15); }
 __device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// One workgroup's work item: KV head g, head group hg and Q tile of sequence
+// bi (items run heaviest Q tile first).  The first sequence's table entries
+// are read together with the scalars the item depends on, so a one-sequence
+// call decodes its item in one round trip to the kernel arguments; later
+// sequences are found by binary search over the cumulative tile counts.
+struct WorkItem {
+  int g, hg, bi, sq, past, slot, q0, kv_start;
+  int64_t tok0;
+};
+template <bool XTRA, bool BATCH>
+__device__ inline WorkItem decode_item(const Params& p, int item) {
+  int n_seq = p.seq.n_seq, n_tiles = p.seq.n_tiles;
+  int h_kv = p.h_kv, n_hg = p.n_hgroups, q_rows = p.q_rows;
+  int cu0 = p.seq.cu_q[0], cu1 = p.seq.cu_q[1], tile0 = 0;
+  WorkItem w;
+  w.past = p.seq.past[0];
+  w.slot = p.seq.slot[0];
+  w.kv_start = p.seq.kv_start[0];
+  // BATCH: every kernel argument the kernel reads before its first global
+  // loads, consumed here at once, so the scalar loads issue as one batch with
+  // one wait (left to itself the scheduler issues them in several batches,
+  // each waited for at its first use) and later reads reuse the values.  The
+  // item's decode takes its operands from the statement, so it cannot be
+  // scheduled between the loads.  (The d = 128 32-key instantiations fail to
+  // compile with these scalar-register operands; they decode without it.)
+  if constexpr (BATCH) {
+    asm volatile(""
+                 : "+s"(n_seq), "+s"(n_tiles), "+s"(h_kv), "+s"(n_hg), "+s"(q_rows)
+                 : "s"(p.scale_log2), "s"(cu0), "s"(cu1), "s"(w.past), "s"(w.slot), "s"(p.h_q),
+                   "s"(p.group), "s"(p.hpack), "s"(p.s_cap), "s"(p.window), "s"(p.q), "s"(p.k),
+                   "s"(p.v), "s"(p.sink));
+    if constexpr (XTRA)
+      asm volatile("" ::"s"(w.kv_start), "s"(p.causal), "s"(p.n_split), "s"(p.kv_idx),
+                   "s"(p.kv_row_bytes), "s"(p.n_pool));
+  }
+  w.g = item % h_kv;
+  const int r0 = item / h_kv;
+  w.hg = r0 % n_hg;
+  const int tix = n_tiles - 1 - r0 / n_hg;
+  w.bi = 0;
+  if (n_seq > 1) {
+    int lo = 0, hi = n_seq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq.cu_tiles[mid] <= tix) lo = mid; else hi = mid - 1;
+    }
+    w.bi = lo;
+    if (lo > 0) {
+      cu0 = p.seq.cu_q[lo];
+      cu1 = p.seq.cu_q[lo + 1];
+      tile0 = p.seq.cu_tiles[lo];
+      w.past = p.seq.past[lo];
+      w.slot = p.seq.slot[lo];
+      w.kv_start = p.seq.kv_start[lo];
+    }
+  }
+  w.sq = cu1 - cu0;
+  w.tok0 = cu0;
+  w.q0 = (tix - tile0) * q_rows;
+  return w;
+}
+
+// Stand-in sink logit for calls without sinks (exp2 of -inf adds nothing).
+__device__ const float g_no_sink = -__builtin_inff();
+typedef __attribute__((address_space(1))) const float global_f32;
+// The row's sink logit, read through a global (not flat) load: a flat load
+// would also count against the LDS/scalar-memory counter, so the next wait on
+// that counter would stall on it.
+__device__ inline float load_sink(const float* sink, int head) {
+  const float* ptr = sink != nullptr ? sink + head : &g_no_sink;
+  return *(const global_f32*)ptr;
+}
+
+// Q fragments as the MFMAs take them: zero for rows past the chunk; fp16 Q
+// pre-scaled by scale * log2 e (one fp16 rounding), so that S comes out of
+// the MFMA in exp2 units; bf16 Q as loaded.
+template <typename TI, int KSTEPS>
+__device__ inline void prepare_q(u32x4* qf, float c, bool valid) {
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    if constexpr (TI::kPrescaleQ) {
+      const f16x8 h8 = __builtin_bit_cast(f16x8, qf[kk]);
+      f16x8 o8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = (_Float16)((float)h8[e] * c);
+      qf[kk] = __builtin_bit_cast(u32x4, o8);
+    }
+    if (!valid) qf[kk] = u32x4{0, 0, 0, 0};
+  }
+}
+
 // Final epilogue of one row (each lane holds half of the row's output
 // columns).  XTRA: compiled with the log-sum-exp output and the split
 // partials (the plain instantiations carry neither).  m_run: the row's reference max in log2 units of the scaled
-// scores; l_kept: its full sum of P over the kept keys (both lane halves).
+// scores; l_kept: its full sum of P over the kept keys (both lane halves);
+// sink: the head's sink logit, or -inf without sinks.
 //   n_split == 1: out = acc / (l_kept + exp2(sink - m)), converted to the
 //     output type; with p.lse, the row's log-sum-exp (natural log, sink
 //     excluded) = (m + log2 l_kept) ln 2.
@@ -233,7 +325,7 @@ __device__ inline float vmax(float a, float b) { return __builtin_elementwise_ma
 //     when this part of the KV range kept no key of the row.
 template <int D, bool XTRA, typename TI, typename TO>
 __device__ inline void finish_row(const Params& p, const f32x16* acc, float m_run, float l_kept,
-                                  int64_t tok, int head, int half) {
+                                  float sink, int64_t tok, int head, int half) {
   constexpr int DB = D / 32;
   const float kNegInf = -__builtin_inff();
   const int64_t row = tok * p.h_q + head;
@@ -255,7 +347,7 @@ __device__ inline void finish_row(const Params& p, const f32x16* acc, float m_ru
     return;
   }
   float l_tot = l_kept;
-  if (p.sink != nullptr && any) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
+  if (any) l_tot += __builtin_amdgcn_exp2f(sink * kLog2e - m_run);  // exp2(-inf) = 0: no sink
   const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
   const int64_t ooff = row * D;
 #pragma unroll
@@ -346,25 +438,11 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   const int col = lane & 31;
 
   // ---- work item: (KV head, head group, Q tile), heaviest Q tiles first ----
-  const int item = blockIdx.x;
-  const int g = item % p.h_kv;
-  const int r0 = item / p.h_kv;
-  const int hg = r0 % p.n_hgroups;
-  const int tix = p.seq.cu_tiles[p.seq.n_seq] - 1 - r0 / p.n_hgroups;
-  int bi = 0;
-  {
-    int lo = 0, hi = p.seq.n_seq - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.seq.cu_tiles[mid] <= tix) lo = mid; else hi = mid - 1;
-    }
-    bi = lo;
-  }
-  const int sq = p.seq.cu_q[bi + 1] - p.seq.cu_q[bi];
-  const int past = p.seq.past[bi];
-  const int slot = p.seq.slot[bi];
-  const int64_t tok0 = p.seq.cu_q[bi];
-  const int q0 = (tix - p.seq.cu_tiles[bi]) * p.q_rows;
+  const WorkItem wi = decode_item<XTRA, D == 64>(p, blockIdx.x);
+  const int g = wi.g, hg = wi.hg, bi = wi.bi;
+  const int sq = wi.sq, past = wi.past, slot = wi.slot;
+  const int64_t tok0 = wi.tok0;
+  const int q0 = wi.q0;
   const int q_last = min(q0 + p.q_rows, sq) - 1;
   const int skv = past + sq;
   const int window = WIN ? p.window : 0;  // compile-time 0 for full attention
@@ -399,30 +477,25 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   const float c = p.scale_log2;
   const float kNegInf = -__builtin_inff();
 
-  // ---- Q^T fragments (B operand), held for the whole KV loop ----
+  // ---- Q^T fragments (B operand), held for the whole KV loop; loaded
+  // here without a branch (rows past the chunk read its last row), then
+  // zeroed where invalid and pre-scaled once the first K/V loads are also in
+  // flight, so that the two round trips overlap ----
   u32x4 qf[KSTEPS];
   {
-    const int64_t qoff = ((tok0 + pos) * p.h_q + head) * D + half * 8;
+    const int64_t qoff = ((tok0 + (valid ? pos : sq - 1)) * p.h_q + head) * D + half * 8;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const u32x4 v = valid ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
-      if constexpr (TI::kPrescaleQ) {
-        const f16x8 h8 = __builtin_bit_cast(f16x8, v);
-        f16x8 o8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = (_Float16)((float)h8[e] * c);
-        qf[kk] = __builtin_bit_cast(u32x4, o8);
-      } else {
-        qf[kk] = v;
-      }
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = load16<TI>(p.q, qoff + kk * 16);
   }
+  // the row's sink, read now (no branch, no use before the epilogue) so
+  // that its latency hides behind the KV loop
+  const float sink = load_sink(p.sink, head);
 
   // Token-pool layout (split/lse variant only): key k of this sequence is
   // pool row kv_list[k], rows h_kv * d elements apart; otherwise the dense
   // cache of this sequence's slot and KV head.
   const bool paged = XTRA && p.kv_idx != nullptr;
-  const int32_t* kv_list = paged ? p.kv_idx + p.seq.kv_start[bi] : nullptr;
+  const int32_t* kv_list = paged ? p.kv_idx + wi.kv_start : nullptr;
   const int64_t kv_base =
       paged ? (int64_t)g * D : ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
   const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
@@ -651,6 +724,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
 #pragma unroll
     for (int s2 = 0; s2 < KD; ++s2) load_kv(pro_k(s2), pro_v(s2));
   }
+  prepare_q<TI, KSTEPS>(qf, c, valid);
   wait_older(issues(pro_k(KD - 1), pro_v(KD - 1)));
   __syncthreads();
 
@@ -787,7 +861,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   // ---- epilogue: combine lane halves, fold the sink, normalise, store ----
   if (sp == 0) {
     const float l_kept = l_run + other_half(l_run);
-    if (valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_kept, tok0 + pos, head, half);
+    if (valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_kept, sink, tok0 + pos, head, half);
   }
 
   if (p.log != nullptr && tid == 0) {
@@ -847,25 +921,11 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   const int col = lane & 31;
 
   // ---- work item: (KV head, head group, Q tile), heaviest Q tiles first ----
-  const int item = blockIdx.x;
-  const int g = item % p.h_kv;
-  const int r0 = item / p.h_kv;
-  const int hg = r0 % p.n_hgroups;
-  const int tix = p.seq.cu_tiles[p.seq.n_seq] - 1 - r0 / p.n_hgroups;
-  int bi = 0;
-  {
-    int lo = 0, hi = p.seq.n_seq - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.seq.cu_tiles[mid] <= tix) lo = mid; else hi = mid - 1;
-    }
-    bi = lo;
-  }
-  const int sq = p.seq.cu_q[bi + 1] - p.seq.cu_q[bi];
-  const int past = p.seq.past[bi];
-  const int slot = p.seq.slot[bi];
-  const int64_t tok0 = p.seq.cu_q[bi];
-  const int q0 = (tix - p.seq.cu_tiles[bi]) * p.q_rows;
+  const WorkItem wi = decode_item<XTRA, D == 64>(p, blockIdx.x);
+  const int g = wi.g, hg = wi.hg, bi = wi.bi;
+  const int sq = wi.sq, past = wi.past, slot = wi.slot;
+  const int64_t tok0 = wi.tok0;
+  const int q0 = wi.q0;
   const int q_last = min(q0 + p.q_rows, sq) - 1;
   const int skv = past + sq;
   const int window = WIN ? p.window : 0;
@@ -897,29 +957,22 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   const float c = p.scale_log2;
   const float kNegInf = -__builtin_inff();
 
+  // Q^T fragments, loaded without a branch (rows past the chunk read its
+  // last row), zeroed and pre-scaled once the first tiles' loads are in flight
   u32x4 qf[KSTEPS];
   {
-    const int64_t qoff = ((tok0 + pos) * p.h_q + head) * D + half * 8;
+    const int64_t qoff = ((tok0 + (valid ? pos : sq - 1)) * p.h_q + head) * D + half * 8;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const u32x4 v = valid ? load16<TI>(p.q, qoff + kk * 16) : u32x4{0, 0, 0, 0};
-      if constexpr (TI::kPrescaleQ) {
-        const f16x8 h8 = __builtin_bit_cast(f16x8, v);
-        f16x8 o8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = (_Float16)((float)h8[e] * c);
-        qf[kk] = __builtin_bit_cast(u32x4, o8);
-      } else {
-        qf[kk] = v;
-      }
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = load16<TI>(p.q, qoff + kk * 16);
   }
+  // the row's sink, read now (no branch, no use before the epilogue)
+  const float sink = load_sink(p.sink, head);
 
   // Token-pool layout (split/lse variant only): key k of this sequence is
   // pool row kv_list[k], rows h_kv * d elements apart; otherwise the dense
   // cache of this sequence's slot and KV head.
   const bool paged = XTRA && p.kv_idx != nullptr;
-  const int32_t* kv_list = paged ? p.kv_idx + p.seq.kv_start[bi] : nullptr;
+  const int32_t* kv_list = paged ? p.kv_idx + wi.kv_start : nullptr;
   const int64_t kv_base =
       paged ? (int64_t)g * D : ((int64_t)slot * p.h_kv + g) * (int64_t)p.s_cap * D;
   const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
@@ -1232,6 +1285,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     for (int j = 0; j < NS - 1; ++j)
       if (j < n_stages) load_tile(j);
   }
+  prepare_q<TI, KSTEPS>(qf, c, valid);
   {
     const int newest = min(NS - 2, n_stages - 1);
     if (newest - 1 >= 2 && NS == 5)
@@ -1300,7 +1354,8 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     }
   }
 
-  if (grp == 0 && valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_run, tok0 + pos, head, half);
+  if (grp == 0 && valid)
+    finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_run, sink, tok0 + pos, head, half);
 
   if (p.log != nullptr && tid == 0) {
     int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 8;
