@@ -66,6 +66,13 @@ MID = [
     ("g64_mqa", 64, 1, 64, [40], [100], -1, "f16", True),
     ("ragged_f16", 8, 2, 64, [1, 0, 77, 200, 5], [0, 5, 300, 64, 1000], 100, "f16", True),
     ("ragged_bf16_d128", 8, 1, 128, [129, 3, 64], [0, 700, 1], -1, "bf16", True),
+    # an empty first sequence: every work item's sequence is found by the
+    # search past the first table entry
+    ("ragged_first_empty", 8, 2, 64, [0, 45, 0, 130], [5, 0, 7, 200], 64, "f16", True),
+    # more sequences than one launch's table holds (128): the call is split
+    # into launches whose tables start at sequence 128
+    ("ragged_150_seqs", 8, 2, 64, [(7 * i) % 6 for i in range(150)],
+     [(37 * i) % 301 for i in range(150)], 50, "f16", True),
 ]
 
 
