@@ -244,8 +244,9 @@ __device__ inline WorkItem decode_item(const Params& p, int item) {
   // one wait (left to itself the scheduler issues them in several batches,
   // each waited for at its first use) and later reads reuse the values.  The
   // item's decode takes its operands from the statement, so it cannot be
-  // scheduled between the loads.  (The d = 128 32-key instantiations fail to
-  // compile with these scalar-register operands; they decode without it.)
+  // scheduled between the loads.  (Some d = 128 instantiations fail to
+  // compile with these scalar-register operands, so d 128 and d 256 decode
+  // without it.)
   if constexpr (BATCH) {
     asm volatile(""
                  : "+s"(n_seq), "+s"(n_tiles), "+s"(h_kv), "+s"(n_hg), "+s"(q_rows)
