@@ -17,9 +17,11 @@ LIB_PATH = os.environ.get("ATTN_PREFILL_LIB") or os.path.join(_HERE, "libattn_pr
 ATTN_OK, ATTN_DECLINED, ATTN_EINVAL, ATTN_EHIP = 0, -1, -2, -3
 ATTN_F16, ATTN_BF16, ATTN_F32 = 1, 2, 3
 ATTN_FLAG_NONCAUSAL = 1
-ATTN_LOG_FIELDS = 8
+ATTN_LOG_FIELDS = 40
+ATTN_LOG_MAX_WAVES = 8
+ATTN_LOG_WAVES = 16
 LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last",
-              "n_visited")
+              "n_visited", "n_waves", "n_splits", "part", "n_parts")
 
 _DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
 
@@ -129,6 +131,61 @@ def _require(t, name, ndim):
         raise ValueError(f"{name}: unsupported dtype {t.dtype}")
 
 
+def _check_tensors(q, k, v, out, head_sink, n_slots=None, tokens=None, lse=None, extra=()):
+    """Consistency of the tensors of one call, checked before the library is
+    reached (the C ABI receives bare pointers and cannot check them): shapes
+    and dtypes that agree with each other, and every tensor on the GPU.
+    k / v are caches [batch, h_kv, s_cap, d] or pools [n_pool, h_kv, d]."""
+    h_q, d = q.shape[1], q.shape[2]
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out {tuple(out.shape)} must have q's shape {tuple(q.shape)}")
+    if out.dtype not in (q.dtype, torch.float32):
+        raise ValueError(f"out dtype {out.dtype} must be q's ({q.dtype}) or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"k / v dtypes ({k.dtype}, {v.dtype}) must equal q's ({q.dtype})")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
+    if k.shape[-1] != d:
+        raise ValueError(f"head dim of k ({k.shape[-1]}) differs from q's ({d})")
+    if n_slots is not None and k.shape[0] < n_slots:
+        raise ValueError(f"the caches hold {k.shape[0]} sequence slots, {n_slots} needed")
+    if tokens is not None and q.shape[0] != tokens:
+        raise ValueError(f"q has {q.shape[0]} rows, cu_seqlens_q ends at {tokens}")
+    if head_sink is not None:
+        if head_sink.dtype != torch.float32 or not head_sink.is_contiguous():
+            raise ValueError("head_sink must be a contiguous float32 tensor")
+        if head_sink.numel() != h_q:
+            raise ValueError(f"head_sink has {head_sink.numel()} entries, h_q = {h_q}")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[0], h_q)):
+        raise ValueError("lse must be a contiguous float32 tensor [tokens, h_q]")
+    named = [("q", q), ("k", k), ("v", v), ("out", out), ("head_sink", head_sink),
+             ("lse", lse)] + list(extra)
+    for name, t in named:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+
+
+def _tile_log(tile_log):
+    if tile_log is None:
+        return None
+    if (tile_log.dtype != torch.int32 or tile_log.dim() != 2
+            or tile_log.shape[1] != ATTN_LOG_FIELDS or not tile_log.is_contiguous()):
+        raise ValueError(f"tile_log must be a contiguous int32 tensor [capacity, {ATTN_LOG_FIELDS}]")
+    if not tile_log.is_cuda:
+        raise ValueError("tile_log must be a GPU tensor")
+    return TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
+
+
+def _seq_meta(cu_seqlens_q, past_len):
+    nseq = len(past_len)
+    if len(cu_seqlens_q) != nseq + 1:
+        raise ValueError("cu_seqlens_q must have len(past_len) + 1 entries")
+    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
+    pl = (ctypes.c_int32 * max(1, nseq))(*[int(x) for x in past_len])
+    return nseq, cu, pl, int(cu_seqlens_q[-1])
+
+
 def attn_prefill(q, k_cache, v_cache, past_len, window, head_sink, scale, out, stream=None,
                  check=True):
     """One chunk after `past_len` cached keys.  q/out [sq, h_q, d];
@@ -139,8 +196,7 @@ def attn_prefill(q, k_cache, v_cache, past_len, window, head_sink, scale, out, s
     _require(v_cache, "v_cache", 4)
     sq, h_q, d = q.shape
     _, h_kv, s_cap, _ = k_cache.shape
-    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
-        raise ValueError("head_sink must be a contiguous float32 tensor")
+    _check_tensors(q, k_cache, v_cache, out, head_sink, n_slots=1)
     code = lib().attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(past_len), int(window),
                               _ptr(head_sink), float(scale), _ptr(out), sq, h_q, h_kv, d, s_cap,
                               _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream))
@@ -158,18 +214,9 @@ def attn_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, past_len, window, hea
     _require(v_cache, "v_cache", 4)
     _, h_q, d = q.shape
     batch, h_kv, s_cap, _ = k_cache.shape
-    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
-    pl = (ctypes.c_int32 * max(1, len(past_len)))(*[int(x) for x in past_len])
-    nseq = len(past_len)
-    if len(cu_seqlens_q) != nseq + 1:
-        raise ValueError("cu_seqlens_q must have len(past_len) + 1 entries")
-    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
-        raise ValueError("head_sink must be a contiguous float32 tensor")
-    log = None
-    if tile_log is not None:
-        if tile_log.dtype != torch.int32 or tile_log.dim() != 2 or tile_log.shape[1] != 8:
-            raise ValueError("tile_log must be an int32 tensor [capacity, 8]")
-        log = TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
+    nseq, cu, pl, tokens = _seq_meta(cu_seqlens_q, past_len)
+    log = _tile_log(tile_log)
+    _check_tensors(q, k_cache, v_cache, out, head_sink, n_slots=nseq, tokens=tokens)
     code = lib().attn_prefill_varlen(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
         float(scale), _ptr(out), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype],
@@ -198,22 +245,13 @@ def attn_prefill_split(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head
     _require(v_cache, "v_cache", 4)
     tokens, h_q, d = q.shape
     batch, h_kv, s_cap, _ = k_cache.shape
-    nseq = len(past_len)
-    if len(cu_seqlens_q) != nseq + 1:
-        raise ValueError("cu_seqlens_q must have len(past_len) + 1 entries")
-    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
-    pl = (ctypes.c_int32 * max(1, nseq))(*[int(x) for x in past_len])
-    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
-        raise ValueError("head_sink must be a contiguous float32 tensor")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (tokens, h_q)):
-        raise ValueError("lse must be a contiguous float32 tensor [tokens, h_q]")
+    nseq, cu, pl, cu_end = _seq_meta(cu_seqlens_q, past_len)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    log = _tile_log(tile_log)
+    _check_tensors(q, k_cache, v_cache, out, head_sink, n_slots=nseq, tokens=cu_end, lse=lse,
+                   extra=[("workspace", workspace)])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    log = None
-    if tile_log is not None:
-        if tile_log.dtype != torch.int32 or tile_log.dim() != 2 or tile_log.shape[1] != 8:
-            raise ValueError("tile_log must be an int32 tensor [capacity, 8]")
-        log = TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
     code = lib().attn_prefill_split(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
         float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype],
@@ -240,24 +278,18 @@ def attn_prefill_paged(q, k_pool, v_pool, kv_indices, kv_indptr, cu_seqlens_q, p
     _require(v_pool, "v_pool", 3)
     tokens, h_q, d = q.shape
     n_pool, h_kv, _ = k_pool.shape
-    nseq = len(past_len)
-    if len(cu_seqlens_q) != nseq + 1 or len(kv_indptr) != nseq + 1:
-        raise ValueError("cu_seqlens_q and kv_indptr must have len(past_len) + 1 entries")
+    nseq, cu, pl, cu_end = _seq_meta(cu_seqlens_q, past_len)
+    if len(kv_indptr) != nseq + 1:
+        raise ValueError("kv_indptr must have len(past_len) + 1 entries")
     if kv_indices.dtype != torch.int32 or not kv_indices.is_contiguous():
         raise ValueError("kv_indices must be a contiguous int32 tensor")
-    cu = (ctypes.c_int32 * len(cu_seqlens_q))(*[int(x) for x in cu_seqlens_q])
+    if nseq > 0 and kv_indices.numel() < int(kv_indptr[-1]):
+        raise ValueError(f"kv_indices has {kv_indices.numel()} entries, kv_indptr ends at "
+                         f"{int(kv_indptr[-1])}")
+    log = _tile_log(tile_log)
+    _check_tensors(q, k_pool, v_pool, out, head_sink, tokens=cu_end, lse=lse,
+                   extra=[("kv_indices", kv_indices)])
     ip = (ctypes.c_int32 * len(kv_indptr))(*[int(x) for x in kv_indptr])
-    pl = (ctypes.c_int32 * max(1, nseq))(*[int(x) for x in past_len])
-    if head_sink is not None and (head_sink.dtype != torch.float32 or not head_sink.is_contiguous()):
-        raise ValueError("head_sink must be a contiguous float32 tensor")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (tokens, h_q)):
-        raise ValueError("lse must be a contiguous float32 tensor [tokens, h_q]")
-    log = None
-    if tile_log is not None:
-        if tile_log.dtype != torch.int32 or tile_log.dim() != 2 or tile_log.shape[1] != 8:
-            raise ValueError("tile_log must be an int32 tensor [capacity, 8]")
-        log = TileLog(tile_log.data_ptr(), tile_log.shape[0], 0, 0, 0)
     code = lib().attn_prefill_paged(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), int(n_pool), _ptr(kv_indices), ip, cu, pl, nseq,
         int(window), _ptr(head_sink), float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d,

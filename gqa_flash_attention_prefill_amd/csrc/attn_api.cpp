@@ -30,6 +30,9 @@
 #include <tuple>
 #include <vector>
 
+static_assert(attn::kLogFields == ATTN_LOG_FIELDS && attn::kLogMaxWaves == ATTN_LOG_MAX_WAVES,
+              "tile-log layout of the kernels and of the ABI");
+
 namespace {
 
 thread_local std::string g_last_error;

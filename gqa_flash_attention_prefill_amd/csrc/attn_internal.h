@@ -11,6 +11,11 @@ namespace attn {
 // (no device copy), so a larger batch is split into several launches.
 constexpr int kMaxSeq = 128;
 
+// Visited-tile record: int32 fields per record, waves reported per record
+// (the layout is attn_tile_log's, in attn_prefill.h).
+constexpr int kLogFields = 40;
+constexpr int kLogMaxWaves = 8;
+
 struct SeqTable {
   int32_t n_seq;
   int32_t n_tiles;                // cu_tiles[n_seq], also read without indexing

@@ -370,6 +370,91 @@ __device__ inline void finish_row(const Params& p, const f32x16* acc, float m_ru
     p.lse[row] = any ? (m_run + __builtin_amdgcn_logf(l_kept)) * kLn2 : kNegInf;
 }
 
+// Visited-tile record of one workgroup (layout: attn_tile_log in
+// attn_prefill.h).  Each wave reports the first and last tile whose scores it
+// used and how many; the waves meet in LDS and thread 0 writes the record:
+// per wave its own three numbers, and for the work item the union of the
+// waves' tiles.  Wave w serves row group w % R and takes every S-th tile of
+// the range from its offset w / R, so the waves of one offset visit runs of
+// one residue class: their union is counted by merging the R runs (sorted by
+// first tile), two runs joining when the gap between them is at most S.
+template <int R, int S>
+__device__ void write_tile_log(const Params& p, void* lds_raw, int wave, int v_first, int v_last,
+                               int v_count, int slot, int h_first, int q0, int q_last) {
+  constexpr int NW = R * S;
+  static_assert(NW <= kLogMaxWaves, "record holds every wave");
+  int* wl = reinterpret_cast<int*>(lds_raw);
+  __syncthreads();  // every LDS read of the epilogue has finished
+  if ((threadIdx.x & 63) == 0) {
+    wl[3 * wave + 0] = v_first;
+    wl[3 * wave + 1] = v_last;
+    wl[3 * wave + 2] = v_count;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kLogFields;
+  int t_first = 0x7fffffff, t_last = -1, n_visited = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    int a[R], b[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int w = s * R + r;
+      const bool any = wl[3 * w + 2] > 0;
+      a[r] = any ? wl[3 * w + 0] : 0x7fffffff;
+      b[r] = any ? wl[3 * w + 1] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int k = 0; k + 1 < R - i; ++k)
+        if (a[k] > a[k + 1]) {
+          const int ta = a[k], tb = b[k];
+          a[k] = a[k + 1];
+          b[k] = b[k + 1];
+          a[k + 1] = ta;
+          b[k + 1] = tb;
+        }
+    int lo = a[0], hi = b[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+      if (b[r] < 0) continue;  // empty (sorted last)
+      if (a[r] <= hi + S) {
+        hi = max(hi, b[r]);
+      } else {
+        n_visited += (hi - lo) / S + 1;
+        lo = a[r];
+        hi = b[r];
+      }
+    }
+    if (hi >= 0) {
+      n_visited += (hi - lo) / S + 1;
+      t_first = min(t_first, a[0]);
+      t_last = max(t_last, hi);
+    }
+  }
+  rec[0] = slot;
+  rec[1] = h_first;
+  rec[2] = p.hpack;
+  rec[3] = q0;
+  rec[4] = q_last;
+  rec[5] = n_visited > 0 ? t_first : -1;
+  rec[6] = n_visited > 0 ? t_last : -1;
+  rec[7] = n_visited;
+  rec[8] = NW;
+  rec[9] = S;
+  rec[10] = blockIdx.y;
+  rec[11] = gridDim.y;
+#pragma unroll
+  for (int i = 12; i < 16; ++i) rec[i] = 0;
+#pragma unroll
+  for (int w = 0; w < kLogMaxWaves; ++w) {
+    rec[16 + 3 * w + 0] = w < NW ? wl[3 * w + 0] : -1;
+    rec[16 + 3 * w + 1] = w < NW ? wl[3 * w + 1] : -1;
+    rec[16 + 3 * w + 2] = w < NW ? wl[3 * w + 2] : 0;
+  }
+}
+
 // This workgroup's part of the Q tile's KV tiles [t_lo, t_hi] when the range
 // is cut into p.n_split contiguous parts (blockIdx.y); may come out empty.
 __device__ inline void split_range(const Params& p, int* t_lo, int* t_hi) {
@@ -698,7 +783,14 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
     }
   };
 
-  int n_visited = 0, t_first = -1, t_last = -1;  // what the loop walks (tile log)
+  // The tiles whose scores this wave actually uses (visited-tile record):
+  // noted where the softmax consumes a tile, not derived from the bounds.
+  int v_first = -1, v_last = -1, v_count = 0;
+  auto note = [&](int t) {
+    if (v_count == 0) v_first = t;
+    v_last = t;
+    ++v_count;
+  };
 
   // ---- prologue: K of stages 0 .. KD-1 and V of stages 0 .. KD-2 (the
   // first K and V always, later ones if the stage exists); then every one
@@ -732,6 +824,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   f32x16 s_a[NB], s_b[NB];   // scores of the current / next tile, roles alternate
   int t_cur = 0;
   if (wave_tile(0, &t_cur)) {
+    note(t_cur);
     scores(lds + sp * TILE_CH, t_cur, s_a);
     const float mx = prepare(t_cur, s_a);
     rebase(mx, s_a);
@@ -780,15 +873,6 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
     const bool newest = issues(kst, vst);
     load_kv(kst, vst);
     if (paged) fetch_rows(j + 1 + KD < n_stages ? j + 1 + KD : -1, j + KD < n_stages ? j + KD : -1);
-#pragma unroll
-    for (int s2 = 0; s2 < S; ++s2) {
-      const int ts = t_lo + j * S + s2;
-      if (ts <= t_hi) {
-        if (t_first < 0) t_first = ts;
-        t_last = ts;
-        ++n_visited;
-      }
-    }
 
     int t_nxt = 0;
     const bool nxt_ok = wave_tile(j + 1, &t_nxt);
@@ -809,6 +893,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
     to_exp2_units(s_nxt);
     float mx = row_max(s_nxt);
     if (nxt_ok) {
+      note(t_nxt);
       // boundary tile: mask, then the max of what is kept (rare)
       if (!interior(t_nxt)) {
         apply_mask(t_nxt, s_nxt);
@@ -865,17 +950,9 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
     if (valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_kept, sink, tok0 + pos, head, half);
   }
 
-  if (p.log != nullptr && tid == 0) {
-    int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 8;
-    rec[0] = slot;
-    rec[1] = g * p.group + hg * p.hpack;
-    rec[2] = p.hpack;
-    rec[3] = q0;
-    rec[4] = q_last;
-    rec[5] = t_first;
-    rec[6] = t_last;
-    rec[7] = n_visited;
-  }
+  if (p.log != nullptr)
+    write_tile_log<R, S>(p, lds, wave, v_first, v_last, v_count, slot, g * p.group + hg * p.hpack,
+                         q0, q_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1194,6 +1271,14 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       }
   };
 
+  // The tiles whose scores this wave actually uses (visited-tile record)
+  int v_first = -1, v_last = -1, v_count = 0;
+  auto note = [&](int t) {
+    if (v_count == 0) v_first = t;
+    v_last = t;
+    ++v_count;
+  };
+
   // One V phase: softmax of S_{j+1} into P_{j+1}.  P is formed against the
   // current reference max first; only when some row's max moved past the
   // threshold (rare: early tiles, rising scores) is the reference raised,
@@ -1202,6 +1287,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     int t = 0;
     const bool ok = wave_tile(j + 1, &t);
     if (ok) {
+      note(t);
       if constexpr (!TI::kPrescaleQ) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -1315,11 +1401,6 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     wait_tiles(j);
     barrier();
   }
-  // what the loop walked: group-local stages 0 .. n_stages - 1, tiles
-  // t_lo + 2 j + {0, 1} up to t_hi
-  const int n_visited = n_stages > 0 ? t_hi - t_lo + 1 : 0;
-  const int t_first = n_stages > 0 ? t_lo : -1;
-  const int t_last = n_stages > 0 ? t_hi : -1;
   // the last prefetch reads must be done before LDS is reused for the merge
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   if (grp == 0) barrier();
@@ -1358,17 +1439,9 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   if (grp == 0 && valid)
     finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_run, sink, tok0 + pos, head, half);
 
-  if (p.log != nullptr && tid == 0) {
-    int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 8;
-    rec[0] = slot;
-    rec[1] = g * p.group + hg * p.hpack;
-    rec[2] = p.hpack;
-    rec[3] = q0;
-    rec[4] = q_last;
-    rec[5] = t_first;
-    rec[6] = t_last;
-    rec[7] = n_visited;
-  }
+  if (p.log != nullptr)
+    write_tile_log<R, 2>(p, lds, wave, v_first, v_last, v_count, slot, g * p.group + hg * p.hpack,
+                         q0, q_last);
 }
 
 template <int D, int BKV, int NS, bool XTRA, typename TI, typename TO>
@@ -1495,18 +1568,49 @@ constexpr KernelConfig make_pp_config(const char* name) {
         {launch<256, 32, 4, 1, 3, BF16, uint16_t>, launch<256, 32, 4, 1, 3, BF16, float>}}}};
 }
 
-const KernelConfig kConfigs[] = {
-    make_pp_config<64, 4>("pp_r128_kv64_ring4"),
-    make_config<64, 4, 2, 4>("r128_kv64_s2_ring4"),
-    make_config<64, 4, 2>("r128_kv64_s2"),
-    make_config<64, 4, 1>("r128_kv64_s1"),
-    make_config<32, 2, 2>("r64_kv32_s2"),
-    // 32-row Q tiles (one row group, two KV-split waves, 48 KB of LDS) for
-    // calls with few rows per sequence, e.g. decode steps (one position x the
-    // KV group's heads)
-    make_config<32, 1, 2>("r32_kv32_s2"),
-};
+}  // namespace
 
+#if defined(ATTN_CONFIG) && ATTN_CONFIG >= 0
+// The library is compiled from this file once per kernel configuration
+// (ATTN_CONFIG = its index in the table below), so that the configurations'
+// instantiations build in parallel; ATTN_CONFIG = -1 compiles the table, the
+// merge kernel and the lookups.
+// (Each entry is a host function, so the device pass never sees the table.)
+#define ATTN_CONFIG_ENTRY(i, ...)                     \
+  const KernelConfig& config_entry_##i() {            \
+    static constexpr KernelConfig entry = __VA_ARGS__; \
+    return entry;                                      \
+  }
+#if ATTN_CONFIG == 0
+ATTN_CONFIG_ENTRY(0, make_pp_config<64, 4>("pp_r128_kv64_ring4"))
+#elif ATTN_CONFIG == 1
+ATTN_CONFIG_ENTRY(1, make_config<64, 4, 2, 4>("r128_kv64_s2_ring4"))
+#elif ATTN_CONFIG == 2
+ATTN_CONFIG_ENTRY(2, make_config<64, 4, 2>("r128_kv64_s2"))
+#elif ATTN_CONFIG == 3
+ATTN_CONFIG_ENTRY(3, make_config<64, 4, 1>("r128_kv64_s1"))
+#elif ATTN_CONFIG == 4
+ATTN_CONFIG_ENTRY(4, make_config<32, 2, 2>("r64_kv32_s2"))
+#elif ATTN_CONFIG == 5
+// 32-row Q tiles (one row group, two KV-split waves, 48 KB of LDS) for calls
+// with few rows per sequence, e.g. decode steps (one position x the KV
+// group's heads)
+ATTN_CONFIG_ENTRY(5, make_config<32, 1, 2>("r32_kv32_s2"))
+#else
+#error "ATTN_CONFIG out of range"
+#endif
+
+#else  // the table, the merge kernel and the lookups
+
+const KernelConfig& config_entry_0();
+const KernelConfig& config_entry_1();
+const KernelConfig& config_entry_2();
+const KernelConfig& config_entry_3();
+const KernelConfig& config_entry_4();
+const KernelConfig& config_entry_5();
+namespace {
+const KernelConfig& (*const kConfigs[])() = {config_entry_0, config_entry_1, config_entry_2,
+                                             config_entry_3, config_entry_4, config_entry_5};
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& mp, int out_is_f32, int out_is_bf16,
@@ -1526,7 +1630,8 @@ hipError_t launch_merge(const MergeParams& mp, int out_is_f32, int out_is_bf16,
 }
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
-const KernelConfig& config(int i) { return kConfigs[i]; }
+const KernelConfig& config(int i) { return kConfigs[i](); }
 int default_config(int /*d*/, int /*dtype*/, int /*window*/) { return 0; }
+#endif
 
 }  // namespace attn

@@ -30,9 +30,10 @@
  *      q, out            [tokens, h_q, d]        tokens = sum of chunk lengths
  *      k_cache, v_cache  [batch, h_kv, s_cap, d]
  *    The caller has already written the chunk's own keys/values at cache
- *    positions [past_len[b], past_len[b] + sq_b); the library only reads the
- *    cache positions [0, past_len[b] + sq_b) of sequence b and never reads a
- *    position at or beyond that (positions up to s_cap may hold anything).
+ *    positions [past_len[b], past_len[b] + sq_b).  A call computes from the
+ *    cache positions [0, past_len[b] + sq_b) of sequence b only; apart from
+ *    the tuning sweep below, it reads no other position (positions up to
+ *    s_cap may hold anything, NaN included).
  *  - head_sink: device float32 [h_q] sink logits in the units of the scaled
  *    scores, or NULL for no sink.  An entry of -INFINITY disables the sink
  *    for that head.
@@ -42,6 +43,19 @@
  *    on it and the call returns without synchronising, except the first call
  *    for a new tuning key, which runs a synchronous tuning sweep on that
  *    stream (see attn_tune_stats).
+ *  - The tuning sweep (first call of a new key only; none when
+ *    ATTN_PREFILL_TUNE=0 or a configuration is forced) times every kernel
+ *    configuration on the caller's own buffers before the real launch.  To
+ *    time a depth that stands for the deeper calls the key will also serve,
+ *    it runs each sequence of a dense cache over positions
+ *    [0, max(past_len[b] + sq_b, min(s_cap, 16384))) -- still inside the
+ *    caller's allocation, whatever those positions hold -- while token-pool
+ *    calls read only their listed keys.  It writes out (and lse and the split
+ *    workspace) several times, without the sink; the real launch then
+ *    overwrites them, so a successful call returns exactly the result of the
+ *    call as specified.  If the sweep fails (ATTN_EHIP), out, lse and the
+ *    workspace may hold a sweep's values.  Nothing outside the caller's
+ *    buffers is touched and nothing is allocated.
  *  - Return codes: ATTN_OK; ATTN_DECLINED (-1): the request is valid but not
  *    supported (d not 64/128/256, dtype not f16/bf16, out dtype neither the input
  *    dtype nor f32, misaligned pointers, device not gfx950) -- nothing is
@@ -67,17 +81,35 @@ enum { ATTN_OK = 0, ATTN_DECLINED = -1, ATTN_EINVAL = -2, ATTN_EHIP = -3 };
 enum { ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_F32 = 3 };
 enum { ATTN_FLAG_NONCAUSAL = 1 };  /* attn_prefill_split / attn_prefill_paged flags */
 
-/* Fields of one visited-tile record (int32 each). */
+/* Fields of one visited-tile record (int32 each).  Every number in fields
+ * 5..7 and in the per-wave fields is observed: each wave notes the tiles whose
+ * scores its softmax actually consumed, and the record's union is formed from
+ * those notes after the loop (never from the floor / ceiling formula). */
 enum {
   ATTN_LOG_B = 0,        /* sequence index                                   */
   ATTN_LOG_H_FIRST = 1,  /* first q head of the work item                    */
-  ATTN_LOG_N_HEADS = 2,  /* q heads the work item covers (h_first ...)       */
+  ATTN_LOG_N_HEADS = 2,  /* q heads the work item covers (h_first ...); the
+                            Q tile's rows are (position, head) pairs, row r =
+                            position q_first + r / n_heads, head
+                            h_first + r % n_heads                            */
   ATTN_LOG_Q_FIRST = 3,  /* first chunk row of the Q tile                    */
   ATTN_LOG_Q_LAST = 4,   /* last chunk row of the Q tile (inclusive)         */
-  ATTN_LOG_T_FIRST = 5,  /* first KV tile the loop visited                   */
-  ATTN_LOG_T_LAST = 6,   /* last KV tile the loop visited                    */
-  ATTN_LOG_N_VISITED = 7,/* KV tiles the loop visited                        */
-  ATTN_LOG_FIELDS = 8
+  ATTN_LOG_T_FIRST = 5,  /* lowest KV tile any wave used (-1: none)          */
+  ATTN_LOG_T_LAST = 6,   /* highest KV tile any wave used (-1: none)         */
+  ATTN_LOG_N_VISITED = 7,/* distinct KV tiles some wave used                 */
+  ATTN_LOG_N_WAVES = 8,  /* waves reported below (<= ATTN_LOG_MAX_WAVES)      */
+  ATTN_LOG_N_SPLITS = 9, /* waves per row group: wave w serves Q-tile rows
+                            [32 (w % R), 32 (w % R) + 31], R = n_waves /
+                            n_splits, and takes the tiles t of its range with
+                            (t - range_first) % n_splits == w / R            */
+  ATTN_LOG_PART = 10,    /* KV part of this record (attn_prefill_split)       */
+  ATTN_LOG_N_PARTS = 11, /* KV parts per Q tile (n_split; 1 otherwise)       */
+  /* 12..15 reserved (0) */
+  ATTN_LOG_WAVES = 16,   /* wave w: fields 16 + 3w: first tile it used (-1:
+                            none), + 1: last tile it used (-1: none), + 2: how
+                            many tiles it used                               */
+  ATTN_LOG_MAX_WAVES = 8,
+  ATTN_LOG_FIELDS = 40
 };
 
 /*
@@ -88,7 +120,8 @@ enum {
  * its sequence.
  *   records   device int32 [capacity * ATTN_LOG_FIELDS], caller-owned
  *   capacity  records available; tokens * h_q always suffices
- *   n_records out: records written (one per work item, in no set order)
+ *   n_records out: records written (one per work item and KV part, in no
+ *             set order)
  *   bkv       out: keys per KV tile
  *   q_rows    out: chunk rows per Q tile
  */
@@ -221,8 +254,8 @@ const char* attn_last_error(void);
  * caller's stream, without the sink) and keeps the fastest; later calls with
  * the same key reuse it.  Since the key leaves out the KV depth, the sweep
  * times every sequence at depth max(past_len, min(s_cap, 16384) - sq) of the
- * caller's cache, so that the choice made on a shallow first chunk holds for
- * the deep ones.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and uses the
+ * caller's cache (see "The tuning sweep" above), so that the choice made on a
+ * shallow first chunk holds for the deep ones.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and uses the
  * default configuration; ATTN_PREFILL_CONFIG=<name> forces one.
  */
 int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys);

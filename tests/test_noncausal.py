@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from gqa_flash_attention_prefill_amd import binding, synth
-from parity_helpers import TOL, f64, rel_l2, to_device
+from parity_helpers import TOL, check_tile_log, f64, new_log, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +46,8 @@ def test_noncausal_matches_oracle(case, n_split):
     for cfg in _each_config():
         out = torch.full(dev["q"].shape, float("nan"), dtype=torch.float32, device="cuda")
         lse = torch.full((tokens, h_q), float("nan"), dtype=torch.float32, device="cuda")
-        log = torch.full((4096, 8), -7, dtype=torch.int32, device="cuda")
-        _, n, bkv, _ = binding.attn_prefill_split(
+        log = new_log(4096, "cuda")
+        _, n, bkv, q_rows = binding.attn_prefill_split(
             dev["q"], dev["k_cache"], dev["v_cache"], dev["cu_seqlens"], dev["past_len"],
             case.window, dev["sink"], case.scale, out, lse=lse, n_split=n_split, workspace=ws,
             tile_log=log, causal=False)
@@ -55,16 +55,9 @@ def test_noncausal_matches_oracle(case, n_split):
         name = binding.attn_config_name(cfg)
         assert rel_l2(f64(out), ref) <= TOL, (name, rel_l2(f64(out), ref))
         assert np.abs(f64(lse) - ref_lse).max() <= 2e-3, name
-        recs = log[:n].cpu().numpy()
-        cu, past = inp["cu_seqlens"], inp["past_len"]
-        for rec in recs:
-            b, _, _, q0, q1, tf, tl, nv = (int(x) for x in rec)
-            skv = past[b] + cu[b + 1] - cu[b]
-            if n_split == 1:
-                lo_key = 0 if case.window <= 0 else max(0, past[b] + q0 - case.window + 1)
-                assert (tf, tl) == (lo_key // bkv, (skv - 1) // bkv), (name, rec)
-            else:
-                assert nv == 0 or tl <= (skv - 1) // bkv
+        # every Q tile walks up to the last key's tile (no causal ceiling)
+        check_tile_log(log[:n].cpu().numpy(), bkv, q_rows, inp["cu_seqlens"], inp["past_len"],
+                       case.window, case.h_q, causal=False)
 
 
 def test_noncausal_differs_from_causal():

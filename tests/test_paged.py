@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from gqa_flash_attention_prefill_amd import binding, synth
-from parity_helpers import TOL, check_tile_log, f64, rel_l2, to_device
+from parity_helpers import TOL, check_tile_log, f64, new_log, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -70,7 +70,7 @@ def _lse_out(dev, out_dtype):
     tokens, h_q, _ = dev["q"].shape
     out = torch.full(dev["q"].shape, float("nan"), dtype=out_dtype, device="cuda")
     lse = torch.full((tokens, h_q), float("nan"), dtype=torch.float32, device="cuda")
-    log = torch.full((4096, 8), -7, dtype=torch.int32, device="cuda")
+    log = new_log(4096, "cuda")
     return out, lse, log
 
 

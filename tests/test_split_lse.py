@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from gqa_flash_attention_prefill_amd import binding, synth
-from parity_helpers import TOL, f64, rel_l2, to_device
+from parity_helpers import TOL, check_tile_log, f64, new_log, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +44,7 @@ def _run(dev, n_split, out_dtype=torch.float32, log_capacity=0):
     lse = torch.full((tokens, h_q), float("nan"), dtype=torch.float32, device=q.device)
     nbytes = binding.attn_split_workspace_bytes(tokens, h_q, d, n_split)
     ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32, device=q.device)
-    log = None
-    if log_capacity:
-        log = torch.full((log_capacity, 8), -7, dtype=torch.int32, device=q.device)
+    log = new_log(log_capacity, q.device) if log_capacity else None
     res = binding.attn_prefill_split(q, dev["k_cache"], dev["v_cache"], dev["cu_seqlens"],
                                      dev["past_len"], dev["window"], dev["sink"], dev["scale"],
                                      out, lse=lse, n_split=n_split, workspace=ws, tile_log=log)
@@ -107,32 +105,15 @@ def test_more_splits_than_tiles_and_dtype_outputs():
 
 @pytest.mark.parametrize("n_split", [1, 3])
 def test_split_tile_log_partitions_the_tile_range(n_split):
-    case = CASES[4]
-    inp = synth.make(case)
-    dev = to_device(inp)
-    tokens, h_q = inp["q"].shape[0], case.h_q
-    for cfg in _each_config():
-        _, _, (recs, bkv, q_rows) = _run(dev, n_split, log_capacity=4096)
-        cu, past = inp["cu_seqlens"], inp["past_len"]
-        parts = {}
-        for rec in recs:
-            b, h0, nh, q0, q1, tf, tl, n = (int(x) for x in rec)
-            parts.setdefault((b, h0, q0, q1), []).append((tf, tl, n))
-        cover = np.zeros((tokens, h_q), dtype=np.int64)
-        for (b, h0, q0, q1), ps in parts.items():
-            assert len(ps) == n_split
-            lo, hi = oracle.tile_range(past[b], q0, q1, inp["window"], bkv)
-            seen = []
-            for tf, tl, n in ps:
-                if n == 0:
-                    continue
-                assert n == tl - tf + 1
-                seen += list(range(tf, tl + 1))
-            assert sorted(seen) == list(range(lo, hi + 1)), (b, q0, ps, lo, hi)
-        for (b, h0, q0, q1), ps in parts.items():
-            nh = int(recs[0][2])
-            cover[cu[b] + q0:cu[b] + q1 + 1, h0:h0 + nh] += 1
-        assert np.all(cover == 1)
+    # every wave of every part reports the tiles it used; the parts of a Q
+    # tile partition the oracle's tile range (check_tile_log)
+    for case in (CASES[4], CASES[1], CASES[3]):
+        inp = synth.make(case)
+        dev = to_device(inp)
+        for cfg in _each_config():
+            _, _, (recs, bkv, q_rows) = _run(dev, n_split, log_capacity=8192)
+            check_tile_log(recs, bkv, q_rows, inp["cu_seqlens"], inp["past_len"], inp["window"],
+                           case.h_q)
 
 
 def test_tp4_rank_long_prefix_sampled_rows():
