@@ -10,13 +10,18 @@ chunk-major (chunk c through all 24 layers, then chunk c + 1), as a model's
 chunked prefill does.
 
 Reported: useful TFLOP/s over the whole step (useful = 4 * d * H_q per kept
-(query, key) pair; masked work in visited tiles does not count), the full-
-attention layers' TFLOP/s and fraction of the MI355X dense fp16/bf16 MFMA
-peak, and microseconds per layer call, from HIP events recorded around every
-launch on the launch stream inside the timed region.  Beside it: the CPU
-oracle's throughput on a bounded row sample of the same workload.
+(query, key) pair; masked work in visited tiles does not count) from the host
+clock around K back-to-back steps; the full-attention layers' TFLOP/s and
+fraction of the MI355X dense fp16/bf16 MFMA peak, and microseconds per layer
+call, from HIP events recorded around every launch on the launch stream in E
+further steps; median / min / p90 of the per-step times, of the per-layer
+times (12 layers x E samples per layer type) and of the first and last
+chunk's calls; the cold first call of each layer type (its tuning sweep
+included).  Beside it: the CPU oracle's throughput on a bounded row sample of
+the same workload, and one whole call of the oracle single-threaded.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--event-steps E]
+       python bench.py --ab OTHER_BUILD.so   (interleaved A/B/A of two builds)
 """
 import argparse
 import csv
@@ -115,10 +120,81 @@ def cpu_baseline(torch, layers_cpu, budget_s=12.0):
     f, s = run(64)
     n = int(np.clip(64 * budget_s / max(s, 1e-3), 64, 200000))
     f, s = run(n)
+
+    # one whole call of the workload, single-threaded: chunk 0 of a window
+    # layer (512 rows, no prefix, window 128)
+    case, a = prepared[1]
+    t0 = time.perf_counter()
+    oracle.attn_prefill_varlen(a["q"][:CHUNK], a["k"], a["v"], [0, CHUNK], [0], case.window,
+                               a["sink"], case.scale, threads=1)
+    one_ms = (time.perf_counter() - t0) * 1e3
     return {"value": f / s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} rows x 2 layers (1 full, 1 window-128) drawn uniformly over the "
                       f"16k positions and 64 heads, fp64 oracle, {s:.1f} s",
-            "seconds": round(s, 2)}
+            "seconds": round(s, 2), "cpu_model": cpu_model(),
+            "single_thread_call": {"call": "window-128 layer, chunk 0 (512 rows, past 0)",
+                                   "threads": 1, "ms": round(one_ms, 1)}}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def dist(xs, nd=3):
+    """median / min / p90 / mean of a sample (and its size)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), nd), "min": round(float(a.min()), nd),
+            "p90": round(float(np.percentile(a, 90)), nd), "mean": round(float(a.mean()), nd),
+            "n": int(a.size)}
+
+
+def _load_lib(path):
+    """A library build's attn_prefill through ctypes (for A/B timing)."""
+    L = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    L.attn_prefill.argtypes = [vp, vp, vp, i32, i32, vp, ctypes.c_float, vp, i32, i32, i32, i32,
+                               i32, i32, i32, vp]
+    L.attn_prefill.restype = ctypes.c_int
+    return L
+
+
+def ab_compare(torch, binding, lib_b, rounds, layers_calls):
+    """Interleaved A/B of two builds of the library on the whole 16k step:
+    per round A, B, then A again (the same-variant control), each one step of
+    768 calls between an event pair on the launch stream.  A is the in-tree
+    build, B the given one (both tune their own configurations first)."""
+    A, B = binding.lib(), _load_lib(lib_b)
+    stream = torch.cuda.current_stream()
+
+    def step(L):
+        for _, _, a in layers_calls:
+            if L.attn_prefill(*a) != 0:
+                raise RuntimeError("attn_prefill failed in the A/B run")
+
+    for L in (A, B):
+        step(L)
+        step(L)
+    torch.cuda.synchronize()
+    res = {"a": [], "b": [], "a_control": []}
+    for _ in range(rounds):
+        for key, L in (("a", A), ("b", B), ("a_control", A)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(L)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[key].append(e0.elapsed_time(e1))
+    a, b, c = (np.array(res[k]) for k in ("a", "b", "a_control"))
+    return {"mode": "interleaved A/B/A (A = in-tree build, B = " + os.path.basename(lib_b) + ")",
+            "rounds": rounds, "ms_per_step": {"a": dist(a), "b": dist(b), "a_control": dist(c)},
+            "b_over_a_median": round(float(np.median(b / a)), 4),
+            "control_over_a_median": round(float(np.median(c / a)), 4)}
 
 
 def kernel_source_hash():
@@ -488,8 +564,14 @@ def configs_demo(torch, binding):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--event-steps", type=int, default=5,
+                    help="steps after the timed ones with an event pair around every call "
+                         "(per-call distributions)")
+    ap.add_argument("--ab", default=None, metavar="LIB_B",
+                    help="interleaved A/B/A timing of the in-tree library against another build")
+    ap.add_argument("--ab-rounds", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-demo", action="store_true",
                     help="time a 64-sequence decode step (prints its own JSON line)")
@@ -574,6 +656,25 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
+    # the first call of each layer type, cold: its tuning sweep runs inside it
+    first = {}
+    for i, (layer, c, _) in enumerate(calls):
+        first.setdefault("full" if layer_window(layer) <= 0 else "window", i)
+    cold_ms = {}
+    for kind in ("full", "window"):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rc = L.attn_prefill(*calls[first[kind]][2])
+        torch.cuda.synchronize()
+        cold_ms[kind] = round((time.perf_counter() - t0) * 1e3, 2)
+        if rc != 0:
+            raise RuntimeError(f"attn_prefill failed: {binding.attn_last_error()} ({rc})")
+    sweeps = binding.attn_tune_stats()
+
+    if args.ab:
+        print(json.dumps(ab_compare(torch, binding, args.ab, args.ab_rounds, calls)), flush=True)
+        return
+
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -581,24 +682,37 @@ def main():
     for kind, w in (("full", -1), ("window", WINDOW)):
         idx = binding.attn_tuned_config(D, torch.float16, torch.float16, CHUNK, H_Q, H_KV, w, 1)
         tuned[kind] = binding.attn_config_name(idx) if idx >= 0 else None
-    print(f"[bench] warmup done; tuning: {binding.attn_tune_stats()}; chosen: {tuned}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] warmup done; tuning: {sweeps}; chosen: {tuned}", file=sys.stderr, flush=True)
 
-    # Timed region: K steps of back-to-back launches.  The last step also
-    # records an event pair around every call on the launch stream (per-call
-    # kernel durations for the breakdown and the roofline); the others carry
-    # no events, since an event pair per call adds ~5 us of queue work to each
-    # launch and would otherwise slow the whole-job figure by ~10 %.
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-          for _ in calls]
+    # Timed region: K steps of back-to-back launches, one event pair per step
+    # on the launch stream (per-step times) and the host clock around all.
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        one_step(ev if s == args.steps - 1 else None)
+        step_ev[s][0].record(stream)
+        one_step()
+        step_ev[s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1000.0 * wall / args.steps
-    dur = np.array([[a.elapsed_time(b) for a, b in ev]])
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms per step", file=sys.stderr,
+          flush=True)
+
+    # Event pass: E more steps with an event pair around every call (an
+    # event pair per call adds queue work, so these steps stay outside the
+    # whole-job figure); per-call kernel times for the breakdown, the
+    # distributions and the roofline.
+    E = max(1, args.event_steps)
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in calls] for _ in range(E)]
+    torch.cuda.synchronize()
+    for e in range(E):
+        one_step(ev[e])
+    torch.cuda.synchronize()
+    dur = np.array([[a.elapsed_time(b) for a, b in ev[e]] for e in range(E)])  # ms
     mean_call = dur.mean(axis=0)
     full_idx = [i for i, (layer, c, _) in enumerate(calls) if layer_window(layer) <= 0]
     win_idx = [i for i, (layer, c, _) in enumerate(calls) if layer_window(layer) > 0]
@@ -615,6 +729,29 @@ def main():
     per_chunk_win = [float(np.mean([mean_call[i] for i in win_idx if calls[i][1] == c])) * 1e3
                      for c in range(N_CHUNKS)]
 
+    def layer_ms(idx):
+        """ms per layer (its 32 chunk calls), one sample per layer and event step."""
+        by_layer = {}
+        for i in idx:
+            by_layer.setdefault(calls[i][0], []).append(i)
+        return [float(dur[e, ids].sum()) for e in range(E) for ids in by_layer.values()]
+
+    def chunk_us(idx, chunk):
+        return [float(dur[e, i]) * 1e3 for e in range(E) for i in idx if calls[i][1] == chunk]
+
+    full_layer = layer_ms(full_idx)
+    distributions = {
+        "step_ms": dist(step_ms),
+        "full_layer_ms": dist(full_layer),
+        "full_layer_frac_peak": dist([full_flops / len(full_layer) * E / (x * 1e-3) / 1e12
+                                      / PEAK_TFLOPS_F16 for x in full_layer], 4),
+        "window_layer_ms": dist(layer_ms(win_idx)),
+        "full_call_us_chunk31": dist(chunk_us(full_idx, N_CHUNKS - 1), 2),
+        "full_call_us_chunk0": dist(chunk_us(full_idx, 0), 2),
+        "window_call_us_chunk31": dist(chunk_us(win_idx, N_CHUNKS - 1), 2),
+        "window_call_us_chunk0": dist(chunk_us(win_idx, 0), 2),
+    }
+
     if args.copy_calibration:
         copy_calibration(torch)
 
@@ -626,7 +763,12 @@ def main():
             cpu_layers.append((case, {k: (v.cpu() if isinstance(v, torch.Tensor) else v)
                                       for k, v in inp.items()}))
         cpu = cpu_baseline(torch, cpu_layers)
+        gpu_us = distributions["window_call_us_chunk0"]["median"]
+        cpu["single_thread_call"]["gpu_us_median"] = gpu_us
+        cpu["single_thread_call"]["ratio"] = round(
+            cpu["single_thread_call"]["ms"] * 1e3 / gpu_us, 1)
 
+    traffic = recorded_traffic()
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -655,6 +797,10 @@ def main():
             "attn_ms_per_16k_prefill": round(full_ms + win_ms, 3),
             "frac_peak_whole_step": round(value / PEAK_TFLOPS_F16, 4),
             "kernel_config": tuned,
+            "distributions": distributions,
+            "event_steps": E,
+            "cold_first_call_ms": {**cold_ms, "tuning_sweeps": sweeps["sweeps"],
+                                   "tuning_launches": sweeps["tuning_launches"]},
         },
         "roofline": {
             "bound": "mfma",
@@ -662,7 +808,12 @@ def main():
             "peak": PEAK_TFLOPS_F16,
             "unit": "TFLOP/s",
             "frac": round(full_tflops / PEAK_TFLOPS_F16, 4),
-            "traffic": recorded_traffic(),
+            "traffic": traffic,
+            "traffic_source": ("recorded, not measured in this run: rocprofv3 FETCH_SIZE + "
+                               "WRITE_SIZE per full-attention launch from "
+                               "profiles/full_attention_16k_traffic.txt, taken on this kernel "
+                               "source (its hash matches)") if traffic is not None else
+                              "null: no counter record matches this kernel source",
             "kernel": "full-attention calls (window <= 0)",
         },
         "cpu_baseline": cpu,

@@ -13,6 +13,14 @@ TOL = 1e-3  # relL2 bound for fp16/bf16 inputs with fp32 accumulation
 # within a few times TOL; a row computed from wrong keys, a wrong head or a
 # wrong position is off by tens of percent.
 ROW_TOL = 4e-3
+# A bf16 output compared with the oracle rounded to bf16 differs only where
+# the two round differently: one bf16 ulp (2^-7 of the element at most) on a
+# row's largest element is a relL2 of up to 2^-7 for that row.
+ROW_TOL_BF16_OUT = 2.0 ** -7
+
+
+def row_tol_for(out_dtype):
+    return ROW_TOL_BF16_OUT if out_dtype == torch.bfloat16 else ROW_TOL
 
 
 def f64(t):
@@ -164,14 +172,14 @@ def row_rel_l2(got, ref):
     return num / np.maximum(den, 1e-300)
 
 
-def check_rows(got, ref, name=""):
-    """Global relL2 <= TOL, and every row's own relL2 <= ROW_TOL."""
+def check_rows(got, ref, name="", row_tol=ROW_TOL):
+    """Global relL2 <= TOL, and every row's own relL2 <= row_tol."""
     err = rel_l2(got, ref)
     rows = row_rel_l2(got, ref)
     worst = float(rows.max()) if rows.size else 0.0
     print(f"{name}: relL2 {err:.3e}, worst row {worst:.3e} over {rows.size} rows", flush=True)
     assert err <= TOL, (name, err)
-    assert worst <= ROW_TOL, (name, worst, np.unravel_index(int(rows.argmax()), rows.shape))
+    assert worst <= row_tol, (name, worst, np.unravel_index(int(rows.argmax()), rows.shape))
     return err, worst
 
 
@@ -181,6 +189,6 @@ def sample_rows(rng, tokens, h_q, n, must=()):
     return np.array(toks, dtype=np.int64), np.array(heads, dtype=np.int32)
 
 
-__all__ = ["TOL", "ROW_TOL", "f64", "rel_l2", "row_rel_l2", "check_rows", "rne", "to_device",
+__all__ = ["TOL", "ROW_TOL", "ROW_TOL_BF16_OUT", "row_tol_for", "f64", "rel_l2", "row_rel_l2", "check_rows", "rne", "to_device",
            "new_log", "run_gpu", "oracle_full", "oracle_rows", "check_tile_log", "sample_rows",
            "synth", "binding"]

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from parity_helpers import (TOL, binding, check_rows, check_tile_log, f64, oracle_full, oracle_rows,
-                            rel_l2, rne, run_gpu, sample_rows, synth, to_device)
+                            rel_l2, rne, row_tol_for, run_gpu, sample_rows, synth, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def _full_check(case, out_dtypes=("same", "f32"), log=True, every_config=False):
             got = f64(out)
             assert np.all(np.isfinite(got)), f"{name}: non-finite output"
             expect = ref if tdt == torch.float32 else rne(ref, tdt)
-            check_rows(got, expect, f"{name} out={od}")
+            check_rows(got, expect, f"{name} out={od}", row_tol=row_tol_for(tdt))
             if log:
                 check_tile_log(recs, bkv, q_rows, case.cu_seqlens, case.past, case.window, case.h_q)
     return ref
@@ -190,7 +190,7 @@ def _whole_check(case, inp=None, q=None, cu=None, past=None, tag=""):
         got = f64(out)
         assert np.all(np.isfinite(got)), name
         expect = ref if tdt == torch.float32 else rne(ref, tdt)
-        check_rows(got, expect, f"{name} whole out={tdt}")
+        check_rows(got, expect, f"{name} whole out={tdt}", row_tol=row_tol_for(tdt))
         check_tile_log(recs, bkv, q_rows, cu, past, case.window, case.h_q)
 
 
@@ -208,7 +208,8 @@ def _sampled_check(case, n_rows=160, seed=0, q=None, cu=None, past=None, inp=Non
         assert torch.isfinite(out).all(), case.name
         got = f64(out)[toks, heads]
         expect = ref if tdt == torch.float32 else rne(ref, tdt)
-        check_rows(got, expect, f"{case.name} {len(toks)} sampled rows out={tdt}")
+        check_rows(got, expect, f"{case.name} {len(toks)} sampled rows out={tdt}",
+                   row_tol=row_tol_for(tdt))
         check_tile_log(recs, bkv, q_rows, cu, past, case.window, case.h_q)
 
 
