@@ -25,7 +25,10 @@ LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last
 
 _DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
 
-EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_split", "attn_prefill_paged",
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+EXPORTED = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_split",
+            "attn_prefill_split_noalloc", "attn_prefill_paged",
             "attn_split_workspace_bytes", "attn_last_error", "attn_tune_stats",
             "attn_tune_reset", "attn_tuned_config", "attn_config_count", "attn_config_name",
             "attn_force_config")
@@ -75,6 +78,11 @@ def lib():
                                      _i32, _i32, _i32, _vp, ctypes.c_int64,
                                      ctypes.POINTER(TileLog), _vp]
     L.attn_prefill_split.restype = ctypes.c_int
+    L.attn_prefill_split_noalloc.argtypes = [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp,
+                                             ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _i32, ctypes.POINTER(TileLog),
+                                             _vp]
+    L.attn_prefill_split_noalloc.restype = ctypes.c_int
     L.attn_prefill_paged.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _vp, _i32p, _i32p, _i32p,
                                      _i32, _i32, _vp, ctypes.c_float, _vp, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _i32, ctypes.POINTER(TileLog), _vp]
@@ -257,6 +265,33 @@ def attn_prefill_split(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head
         float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype],
         _DTYPE_CODE[out.dtype], int(n_split), 0 if causal else ATTN_FLAG_NONCAUSAL,
         _ptr(workspace), int(ws_bytes),
+        ctypes.byref(log) if log is not None else None, _stream(stream))
+    if check:
+        _check(code)
+    if log is not None:
+        return code, log.n_records, log.bkv, log.q_rows
+    return code
+
+
+def attn_prefill_split_noalloc(q, k_cache, v_cache, cu_seqlens_q, past_len, window, head_sink,
+                               scale, out, lse=None, n_split=1, tile_log=None, stream=None,
+                               check=True, causal=True):
+    """attn_prefill_split without a workspace: the KV-split partials go to the
+    library's static device scratch (ATTN_NOALLOC_SCRATCH_BYTES per GPU);
+    nothing is allocated and no tuning sweep runs."""
+    _require(q, "q", 3)
+    _require(out, "out", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    tokens, h_q, d = q.shape
+    batch, h_kv, s_cap, _ = k_cache.shape
+    nseq, cu, pl, cu_end = _seq_meta(cu_seqlens_q, past_len)
+    log = _tile_log(tile_log)
+    _check_tensors(q, k_cache, v_cache, out, head_sink, n_slots=nseq, tokens=cu_end, lse=lse)
+    code = lib().attn_prefill_split_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), cu, pl, nseq, int(window), _ptr(head_sink),
+        float(scale), _ptr(out), _ptr(lse), h_q, h_kv, d, s_cap, _DTYPE_CODE[q.dtype],
+        _DTYPE_CODE[out.dtype], int(n_split), 0 if causal else ATTN_FLAG_NONCAUSAL,
         ctypes.byref(log) if log is not None else None, _stream(stream))
     if check:
         _check(code)

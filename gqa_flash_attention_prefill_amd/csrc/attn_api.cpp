@@ -32,6 +32,8 @@
 
 static_assert(attn::kLogFields == ATTN_LOG_FIELDS && attn::kLogMaxWaves == ATTN_LOG_MAX_WAVES,
               "tile-log layout of the kernels and of the ABI");
+static_assert(attn::kNoallocScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES,
+              "the no-allocation entry point's scratch size");
 
 namespace {
 
@@ -114,6 +116,9 @@ struct Call {
   const int32_t* kv_idx = nullptr;     // device: pool row of each key
   const int32_t* kv_indptr = nullptr;  // host [batch + 1]: sequence b's entries in kv_idx
   int64_t n_pool = 0;
+  // attn_prefill_split_noalloc: the split workspace is the library's static
+  // device scratch, and no tuning sweep runs (a sweep synchronises)
+  bool noalloc = false;
 };
 
 constexpr int32_t kMaxSplit = 64;
@@ -290,6 +295,11 @@ int choose_config(const Call& c, int* cfg) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   auto it = g_tune.find(key);
   if (it != g_tune.end()) { *cfg = it->second; return ATTN_OK; }
+  if (c.noalloc) {
+    // never sweeps: the key's earlier choice (above), else the default
+    *cfg = attn::default_config(c.d, c.dtype, c.window);
+    return ATTN_OK;
+  }
   int best = 0;
   int rc = sweep(c, &best);
   if (rc) return rc;
@@ -341,7 +351,14 @@ int validate(const Call& c) {
   if (c.flags & ~ATTN_FLAG_NONCAUSAL) return fail(ATTN_EINVAL, "unknown flags 0x%x", c.flags);
   if (c.n_split < 1 || c.n_split > kMaxSplit)
     return fail(ATTN_EINVAL, "n_split %d outside 1..%d", c.n_split, kMaxSplit);
-  if (c.n_split > 1 && tokens > 0) {
+  if (c.noalloc && tokens > 0) {
+    const int64_t need = split_workspace_bytes(tokens, c.h_q, c.d, c.n_split);
+    if (need > attn::kNoallocScratchBytes)
+      return fail(ATTN_EINVAL,
+                  "split partials need %lld bytes, above the %lld-byte scratch of the "
+                  "no-allocation entry point (use attn_prefill_split with a workspace)",
+                  (long long)need, (long long)attn::kNoallocScratchBytes);
+  } else if (c.n_split > 1 && tokens > 0) {
     const int64_t need = split_workspace_bytes(tokens, c.h_q, c.d, c.n_split);
     if (!c.workspace || c.workspace_bytes < need)
       return fail(ATTN_EINVAL, "split workspace holds %lld bytes, %lld needed",
@@ -368,18 +385,25 @@ int validate(const Call& c) {
   return ATTN_OK;
 }
 
-int run(const Call& c) {
+int run(const Call& c_in) {
   g_last_error.clear();
-  int rc = validate(c);
+  int rc = validate(c_in);
   if (rc) return rc;
-  const int64_t tokens = c.batch > 0 ? c.cu[c.batch] : 0;
+  const int64_t tokens = c_in.batch > 0 ? c_in.cu[c_in.batch] : 0;
   if (tokens == 0) {
-    if (c.log) { c.log->n_records = 0; }
+    if (c_in.log) { c_in.log->n_records = 0; }
     return ATTN_OK;
   }
   int dev = 0;
   rc = check_device(&dev);
   if (rc) return rc;
+  Call c = c_in;
+  if (c.noalloc && c.n_split > 1) {
+    // the static scratch of this device (its address, looked up once)
+    hipError_t e = attn::noalloc_scratch(&c.workspace);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "scratch address: %s", hipGetErrorString(e));
+    c.workspace_bytes = attn::kNoallocScratchBytes;
+  }
   int cfg = 0;
   rc = choose_config(c, &cfg);
   if (rc) return rc;
@@ -455,6 +479,26 @@ int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
     c.flags = flags;
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
+    return run(c);
+  } catch (...) {
+    return fail(ATTN_EHIP, "internal error");
+  }
+}
+
+int attn_prefill_split_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens_q, const int32_t* past_len,
+                               int32_t batch, int32_t window, const float* head_sink, float scale,
+                               void* out, float* lse, int32_t h_q, int32_t h_kv, int32_t d,
+                               int32_t s_cap, int32_t dtype, int32_t out_dtype, int32_t n_split,
+                               int32_t flags, attn_tile_log* tile_log, void* stream) {
+  try {
+    Call c{q, k_cache, v_cache, out, head_sink, cu_seqlens_q, past_len, batch, window, h_q,
+           h_kv, d, s_cap, dtype, out_dtype, scale, tile_log,
+           reinterpret_cast<hipStream_t>(stream)};
+    c.lse = lse;
+    c.n_split = n_split;
+    c.flags = flags;
+    c.noalloc = true;
     return run(c);
   } catch (...) {
     return fail(ATTN_EHIP, "internal error");

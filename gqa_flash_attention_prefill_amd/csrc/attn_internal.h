@@ -82,6 +82,12 @@ struct KernelConfig {
 // 0: d 64, 1: d 128, 2: d 256
 inline int d_index(int d) { return d == 64 ? 0 : (d == 128 ? 1 : 2); }
 
+// Device scratch of attn_prefill_split_noalloc: a file-scope device array of
+// this many bytes (one copy per GPU, held until the process ends).  Returns
+// its device address on the current device (looked up once per device).
+constexpr int64_t kNoallocScratchBytes = (int64_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 int config_count();
 const KernelConfig& config(int i);
 int default_config(int d, int dtype, int window);

@@ -55,6 +55,7 @@
 
 #include <float.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace attn {
@@ -1627,6 +1628,35 @@ hipError_t launch_merge(const MergeParams& mp, int out_is_f32, int out_is_bf16,
   return out == 2 ? launch_merge_t<256, 2>(mp, stream)
                   : (out == 1 ? launch_merge_t<256, 1>(mp, stream)
                               : launch_merge_t<256, 0>(mp, stream));
+}
+
+// Scratch of attn_prefill_split_noalloc (the KV-split partials of one call),
+// so that callers that cannot allocate need not pass a workspace.  In host
+// code `scratch` names a host-side stand-in, never the device array: its
+// device address is taken once per device with hipGetSymbolAddress (with
+// that device current) and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

@@ -204,6 +204,31 @@ int attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
                        void* stream);
 
 /*
+ * attn_prefill_split without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of attn_prefill_split (without workspace / workspace_bytes).  Differences:
+ *  - The KV-split partials live in the library's own device scratch, a
+ *    file-scope array of ATTN_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held
+ *    until the process ends; a call whose partials,
+ *    attn_split_workspace_bytes(tokens, h_q, d, n_split), exceed it returns
+ *    ATTN_EINVAL before anything is launched.
+ *  - Nothing is allocated or freed, and no tuning sweep runs: the call uses
+ *    the configuration its tuning key already holds, else the default one.
+ *  - All calls on one GPU share that GPU's scratch: calls that may overlap
+ *    in time on one GPU (different streams, different threads) race and must
+ *    be ordered by the caller.  Nothing in the scratch needs to start at
+ *    zero (each call writes every partial it then reads).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+int attn_prefill_split_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens_q, const int32_t* past_len,
+                               int32_t batch, int32_t window, const float* head_sink, float scale,
+                               void* out, float* lse, int32_t h_q, int32_t h_kv, int32_t d,
+                               int32_t s_cap, int32_t dtype, int32_t out_dtype, int32_t n_split,
+                               int32_t flags, attn_tile_log* tile_log, void* stream);
+
+/*
  * Ragged batch over a token-pool KV layout (sglang pull request 34468,
  * "Commit 1": the extend kernel reads the cached prefix through kv_indptr /
  * kv_indices into a pool of token slots, and its window-bounded variant

@@ -164,3 +164,23 @@ def test_paged_entry_validates_before_any_gpu_call():
     # pool offsets are 32-bit: 2^23 rows x 2 heads x 128 x 2 bytes = 4 GiB declines
     assert call([0, 100], 0, n_pool=1 << 23, d=128) == binding.ATTN_DECLINED
     assert call([0, 100], 0, ptr=ctypes.c_void_p(0x10008)) == binding.ATTN_DECLINED
+
+
+def test_noalloc_entry_checks_its_scratch_limit_before_any_gpu_call():
+    L = binding.lib()
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+    tokens = 4096
+    cu = (ctypes.c_int32 * 2)(0, tokens)
+    past = (ctypes.c_int32 * 1)(0)
+
+    def call(n_split, h_q=64):
+        return L.attn_prefill_split_noalloc(fake, fake, fake, cu, past, 1, -1, None,
+                                            ctypes.c_float(0.125), fake, None, h_q, 8, 64, tokens,
+                                            binding.ATTN_F16, binding.ATTN_F16, n_split, 0, None,
+                                            None)
+
+    assert binding.attn_split_workspace_bytes(tokens, 64, 64, 2) > binding.ATTN_NOALLOC_SCRATCH_BYTES
+    assert call(2) == binding.ATTN_EINVAL
+    assert "scratch" in binding.attn_last_error()
+    assert call(0) == binding.ATTN_EINVAL
+    assert call(2, h_q=6) == binding.ATTN_EINVAL   # h_q not a multiple of h_kv
