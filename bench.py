@@ -572,6 +572,8 @@ def main():
     ap.add_argument("--ab", default=None, metavar="LIB_B",
                     help="interleaved A/B/A timing of the in-tree library against another build")
     ap.add_argument("--ab-rounds", type=int, default=10)
+    ap.add_argument("--ab-kind", choices=("all", "full", "window"), default="all",
+                    help="A/B over every call of the step, or only one layer type's calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-demo", action="store_true",
                     help="time a 64-sequence decode step (prints its own JSON line)")
@@ -672,7 +674,11 @@ def main():
     sweeps = binding.attn_tune_stats()
 
     if args.ab:
-        print(json.dumps(ab_compare(torch, binding, args.ab, args.ab_rounds, calls)), flush=True)
+        keep = {"all": lambda w: True, "full": lambda w: w <= 0, "window": lambda w: w > 0}
+        sel = [cl for cl in calls if keep[args.ab_kind](layer_window(cl[0]))]
+        res = ab_compare(torch, binding, args.ab, args.ab_rounds, sel)
+        res["calls"] = f"{args.ab_kind} ({len(sel)} calls per step)"
+        print(json.dumps(res), flush=True)
         return
 
     for _ in range(args.warmup):

@@ -69,6 +69,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -984,6 +985,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   constexpr int DB = D / 32;
   constexpr int LPW = SLOT_CH / 64 / R;     // 1-KB direct loads per wave per tile
   constexpr float kRescale = 8.f;
+  constexpr uint16_t kPsumMax = 0x6400;  // fp16 1024
   static_assert(NS == 4 || NS == 5, "ring of 4 or 5 tiles per group");
   static_assert(NB <= 2, "one -m splat per 32-key block (negm, negm1)");
   static_assert(SLOT_CH % (64 * R) == 0, "direct loads tile a slot");
@@ -1131,9 +1133,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // Row sums of P on the matrix pipe: ones . P^T puts the sum of P over the
   // tile's keys in every element of the row's column (the vector pipe is the
   // busier one at d = 64).  fp16 inputs: the tile's four 16-key P vectors are
-  // first added as packed fp16 (p <= 2^8, so a sum of four stays below
-  // 2^10; one rounding of 2^-11 relative per add), then one MFMA sums them;
-  // bf16 inputs: one MFMA per 16-key step for each of P's two parts.
+  // first added as packed fp16 in the V phase (no sum exceeds 2^10: the V
+  // phase raises the reference max otherwise; one rounding of 2^-11 relative
+  // per add), then one MFMA sums them; bf16 inputs: one MFMA per 16-key step
+  // for each of P's two parts.
   f32x16 lsum = f32x16{};
   const u32x4 ones = {TI::kOnePair, TI::kOnePair, TI::kOnePair, TI::kOnePair};
   f32x16 acc[DB];
@@ -1143,6 +1146,8 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   u32x4 kf[NB][KSTEPS];
   u32x4 vf[DB][NG];
   u32x4 pb[NG], pl[NG];
+  u32x4 psum = {0, 0, 0, 0};  // fp16: the tile's P pre-added (see presum)
+  bool started = false;       // wave-uniform: every row holds a reference max
 #pragma unroll
   for (int g16 = 0; g16 < NG; ++g16) {
     pb[g16] = u32x4{0, 0, 0, 0};
@@ -1208,12 +1213,8 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         lsum = TI::mma(ones, pb[g16], lsum);
         lsum = TI::mma(ones, pl[g16], lsum);
       } else if (g16 == NG - 1) {
-        // fp16 P of the tile's 16-key steps added as whole vectors (packed
-        // fp16 adds), then one row-sum MFMA for the tile
-        f16x8 sum = __builtin_bit_cast(f16x8, pb[0]);
-#pragma unroll
-        for (int g2 = 1; g2 < NG; ++g2) sum += __builtin_bit_cast(f16x8, pb[g2]);
-        lsum = TI::mma(ones, __builtin_bit_cast(u32x4, sum), lsum);
+        // fp16: one row-sum MFMA for the tile over its pre-added P
+        lsum = TI::mma(ones, psum, lsum);
       }
       vf[DB - 1][g16] = v_frag<D>(vt, g16, DB - 1, lane);
     }
@@ -1284,47 +1285,94 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // current reference max first; only when some row's max moved past the
   // threshold (rare: early tiles, rising scores) is the reference raised,
   // O and l rescaled and P formed again.
+  // fp16: the tile's four 16-key P vectors added as packed fp16 (whole-vector
+  // adds), the operand of the tile's one row-sum MFMA in the next M phase
+  auto presum = [&]() {
+    if constexpr (!TI::kSplitP) {
+      f16x8 sum = __builtin_bit_cast(f16x8, pb[0]);
+#pragma unroll
+      for (int g2 = 1; g2 < NG; ++g2) sum += __builtin_bit_cast(f16x8, pb[g2]);
+      psum = __builtin_bit_cast(u32x4, sum);
+    }
+  };
+  // Raise the reference max to the tile's row max where it exceeds it by more
+  // than kRescale (or where the row had none), rescaling O and l, then form P
+  // again; `mx` is the row max of S relative to the current reference.
+  auto rescale = [&](float mx) {
+    const float mx_abs = mx + m_use;
+    const float m_new = fmaxf(m_run, mx_abs);
+    const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    m_run = m_new;
+    const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
+    const float shift = m_use - m_use_new;
+    m_use = m_use_new;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+    negm1 = negm;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[nb][i] += shift;
+    make_p();
+  };
+  // Does some element of the pre-added P exceed 2^10 (or is it inf / NaN)?
+  // Non-negative fp16 values order as their bit patterns.
+  auto psum_big = [&]() {
+    u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, psum[0]),
+                                        __builtin_bit_cast(u16x2, psum[1]));
+    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, psum[2]),
+                                              __builtin_bit_cast(u16x2, psum[3]));
+    a = __builtin_elementwise_max(a, b);
+    return a[0] > kPsumMax || a[1] > kPsumMax;
+  };
+
+  // One V phase: softmax of S_{j+1} into P_{j+1}.
+  //  * fp16, interior tile (no pair masked), every row of the wave already
+  //    holding a reference max: P is formed at once against that reference,
+  //    and the reference is raised only if some pre-added P exceeds 2^10
+  //    (then each p <= 2^10 otherwise, so the fp16 P and its pre-added sums
+  //    stay finite).  No row max is taken on this path.
+  //  * otherwise (boundary tiles, a wave's first tiles, bf16): mask, the row
+  //    max over both lane halves, and a raise of the reference when some
+  //    row's max exceeds it by more than kRescale or a row had none.
   auto v_phase = [&](int j) {
     int t = 0;
     const bool ok = wave_tile(j + 1, &t);
     if (ok) {
       note(t);
+      const bool inner = (t * BKV + BKV - 1 <= w_full_hi) && (t * BKV >= w_full_lo);
+      const bool fast = TI::kPrescaleQ && started && inner;
       if constexpr (!TI::kPrescaleQ) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[nb][i] = __builtin_fmaf(sc[nb][i], c, -m_use);
       }
-      if (!((t * BKV + BKV - 1 <= w_full_hi) && (t * BKV >= w_full_lo))) apply_mask(t);
-      const float mx = pair_max(lane_max());
-      make_p();
-      const bool need = (mx > kRescale) || (m_run == kNegInf && mx != kNegInf);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float mx_abs = mx + m_use;
-        const float m_new = fmaxf(m_run, mx_abs);
-        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        m_run = m_new;
-        const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
-        const float shift = m_use - m_use_new;
-        m_use = m_use_new;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) negm[i] = -m_use;
-        negm1 = negm;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[nb][i] += shift;
-        make_p();
+      float mx = 0.f;
+      if (!fast) {
+        if (!inner) apply_mask(t);
+        mx = pair_max(lane_max());
       }
+      make_p();
+      presum();
+      const bool need = fast ? psum_big()
+                             : (mx > kRescale) || (m_run == kNegInf && mx != kNegInf);
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        if (fast) mx = pair_max(lane_max());
+        rescale(mx);
+        presum();
+      }
+      if (!fast) started = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
     } else {
 #pragma unroll
       for (int g16 = 0; g16 < NG; ++g16) {
         pb[g16] = u32x4{0, 0, 0, 0};
         pl[g16] = u32x4{0, 0, 0, 0};
       }
+      psum = u32x4{0, 0, 0, 0};
     }
   };
   auto barrier = [&]() {
