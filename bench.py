@@ -340,6 +340,138 @@ def one_call(torch, binding, chunk):
     print(f"[bench] one_call chunk {chunk}: 3 launches of the full-attention call", flush=True)
 
 
+CANDIDATE_LAUNCHES = 3
+
+
+def candidate_calls(torch, binding):
+    """The call shapes of the per-configuration counter table: the deepest
+    full-attention chunk of the 16k prefill (512 rows after 15872 keys), a
+    window-128 chunk at mid depth (512 rows after 8192 keys), both fp16 with
+    sinks, and the ragged bf16 d 128 batch of 8 sequences (window 128, bf16
+    out).  Returns [(label, callable)]."""
+    from gqa_flash_attention_prefill_amd import synth
+    out = []
+    for layer, chunk, label in ((0, N_CHUNKS - 1, "full_chunk31"), (1, 16, "window128_chunk16")):
+        case = synth.chunked16k_layer(layer)
+        inp = synth.make(case, device="cuda:0")
+        o = torch.empty_like(inp["q"])
+        q = inp["q"][chunk * CHUNK:(chunk + 1) * CHUNK]
+        oc = o[chunk * CHUNK:(chunk + 1) * CHUNK]
+
+        def call(inp=inp, q=q, oc=oc, chunk=chunk, case=case):
+            binding.attn_prefill(q, inp["k_cache"], inp["v_cache"], chunk * CHUNK, case.window,
+                                 inp["sink"], case.scale, oc)
+        out.append((label, call))
+    rc = synth.ragged_bf16()
+    rc = synth.Case(rc.name, h_q=rc.h_q, h_kv=rc.h_kv, d=rc.d, sq=list(rc.sq), past=list(rc.past),
+                    window=rc.window, dtype=rc.dtype, seed=rc.seed, poison_tail=False)
+    rinp = synth.make(rc, device="cuda:0")
+    rout = torch.empty_like(rinp["q"])
+
+    def ragged():
+        binding.attn_prefill_varlen(rinp["q"], rinp["k_cache"], rinp["v_cache"],
+                                    rinp["cu_seqlens"], rinp["past_len"], rinp["window"],
+                                    rinp["sink"], rc.scale, rout)
+    out.append(("ragged8_bf16_d128", ragged))
+    return out
+
+
+def run_candidates(torch, binding):
+    """Every kernel configuration, forced, on each candidate call shape:
+    CANDIDATE_LAUNCHES launches per (configuration, call), in a fixed order
+    (configurations outer), then the 1 GiB calibration copy.  Under a
+    profiler the attention dispatches come in groups of CANDIDATE_LAUNCHES in
+    the printed order."""
+    torch.cuda.set_device(0)
+    calls = candidate_calls(torch, binding)
+    order = []
+    try:
+        for cfg in range(binding.attn_config_count()):
+            binding.attn_force_config(cfg)
+            for label, fn in calls:
+                for _ in range(CANDIDATE_LAUNCHES):
+                    fn()
+                torch.cuda.synchronize()
+                order.append([binding.attn_config_name(cfg), label])
+    finally:
+        binding.attn_force_config(-1)
+    copy_calibration(torch)
+    print(json.dumps({"candidate_order": order, "launches": CANDIDATE_LAUNCHES}), flush=True)
+
+
+def summarize_candidates(order_file, trace_csv, pmc_dirs):
+    """Per (configuration, call): mean kernel duration over the launches after
+    the first (kernel trace) and the mean of every counter of the PMC passes
+    over the same dispatches; HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by
+    the calibration copy's readings of the same counters."""
+    order = None
+    for line in open(order_file):
+        line = line.strip()
+        if line.startswith("{") and "candidate_order" in line:
+            order = json.loads(line)
+    assert order is not None, "no candidate_order line"
+    n = order["launches"]
+    groups = order["candidate_order"]
+
+    def attn_rows(rows, key_name, key_id):
+        att = [r for r in rows if _classify(r[key_name]) in ("attn_full", "attn_window")]
+        ids = sorted({int(r[key_id]) for r in att})
+        return att, ids
+
+    trace = list(csv.DictReader(open(trace_csv)))
+    att, ids = attn_rows(trace, "Kernel_Name", "Dispatch_Id")
+    assert len(ids) == n * len(groups), (len(ids), n, len(groups))
+    dur = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+           for r in att}
+    names = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in att}
+    table = []
+    for gi, (cfg, label) in enumerate(groups):
+        gid = ids[gi * n:(gi + 1) * n][1:]
+        table.append({"config": cfg, "call": label,
+                      "kernel": names[gid[0]].split("(")[0].replace(
+                          "attn::(anonymous namespace)::", ""),
+                      "us": round(float(np.mean([dur[i] for i in gid])), 2), "counters": {}})
+    copy_vals = {}
+    for d in pmc_dirs:
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += list(csv.DictReader(open(f)))
+        per = {}
+        copies = {}
+        for r in rows:
+            key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+            if _classify(r["Kernel_Name"]) == "copy":
+                copies[key] = copies.get(key, 0.0) + float(r["Counter_Value"])
+            elif _classify(r["Kernel_Name"]) in ("attn_full", "attn_window"):
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        pids = sorted({k[0] for k in per})
+        assert len(pids) == n * len(groups), (d, len(pids))
+        counters = sorted({k[1] for k in per})
+        for (cid, cname), v in copies.items():
+            copy_vals[cname] = max(copy_vals.get(cname, 0.0), v)
+        for gi in range(len(groups)):
+            gid = pids[gi * n:(gi + 1) * n][1:]
+            for cname in counters:
+                table[gi]["counters"][cname] = float(np.mean([per[(i, cname)] for i in gid]))
+    kib = COPY_BYTES / 1024.0
+    for row in table:
+        c = row["counters"]
+        if "FETCH_SIZE" in c and copy_vals.get("FETCH_SIZE"):
+            row["hbm_read_mb"] = round(c["FETCH_SIZE"] * kib / copy_vals["FETCH_SIZE"] * 1024 / 1e6, 2)
+        if "WRITE_SIZE" in c and copy_vals.get("WRITE_SIZE"):
+            row["hbm_write_mb"] = round(c["WRITE_SIZE"] * kib / copy_vals["WRITE_SIZE"] * 1024 / 1e6, 2)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
+            # 256 CUs x 4 SIMDs over the XCDs' active cycles (8 XCDs)
+            row["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                     (1024 * c["GRBM_GUI_ACTIVE"] / 8), 4)
+            row["clock_ghz"] = round(c["GRBM_GUI_ACTIVE"] / 8 / (row["us"] * 1e3), 3)
+        if "SQ_INSTS_VALU" in c and c.get("SQ_INSTS_MFMA"):
+            row["valu_per_mfma"] = round(c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"], 2)
+        if "TCC_HIT" in c and "TCC_MISS" in c:
+            row["l2_hit"] = round(c["TCC_HIT"] / max(1.0, c["TCC_HIT"] + c["TCC_MISS"]), 4)
+    return {"copy_calibration": copy_vals, "rows": table}
+
+
 def _time_calls(torch, binding, args, reps=20):
     """Mean us per call of `reps` back-to-back attn_prefill_split calls with
     pre-marshalled arguments, between one event pair on the launch stream
@@ -593,11 +725,21 @@ def main():
     ap.add_argument("--one-call", type=int, default=None, metavar="CHUNK",
                     help="only run the full-attention call of chunk CHUNK (3 times, untimed), "
                          "for hardware-counter passes on one launch shape")
+    ap.add_argument("--candidates", action="store_true",
+                    help="every configuration, forced, on the counter-table call shapes "
+                         "(for rocprofv3 passes; prints the dispatch order)")
+    ap.add_argument("--summarize-candidates", nargs="+", default=None,
+                    metavar="ARG", help="ORDER_LOG KERNEL_TRACE_CSV PMC_DIR... -> the "
+                                        "per-configuration table (JSON)")
     ap.add_argument("--summarize-pmc", default=None, metavar="PMC_DIR",
                     help="per-dispatch averages of every counter of the attention kernels")
     args = ap.parse_args()
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
+    if args.summarize_candidates:
+        a = args.summarize_candidates
+        print(json.dumps(summarize_candidates(a[0], a[1], a[2:]), indent=1))
         return
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
@@ -617,6 +759,9 @@ def main():
     L = binding.lib()
     if args.one_call is not None:
         one_call(torch, binding, args.one_call)
+        return
+    if args.candidates:
+        run_candidates(torch, binding)
         return
     if args.split_demo or args.decode_demo or args.paged_demo or args.configs_demo:
         torch.cuda.set_device(0)

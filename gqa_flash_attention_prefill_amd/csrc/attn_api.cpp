@@ -372,6 +372,12 @@ int validate(const Call& c) {
   if (c.out_dtype != c.dtype && c.out_dtype != ATTN_F32)
     return fail(ATTN_DECLINED, "out dtype %d not supported for input dtype %d", c.out_dtype,
                 c.dtype);
+  // fp16 q is pre-scaled by scale * log2 e in fp16; |q| <= 65504, so the
+  // product stays finite exactly when |scale| * log2 e <= 1
+  if (c.dtype == ATTN_F16 && std::fabs((double)c.scale) * 1.4426950408889634 > 1.0)
+    return fail(ATTN_DECLINED,
+                "fp16 inputs with |scale| > ln 2 (%g): the pre-scaled fp16 q could overflow",
+                (double)c.scale);
   if (tokens > 0) {
     auto mis = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; };
     if (mis(c.q) || mis(c.k) || mis(c.v) || mis(c.out))

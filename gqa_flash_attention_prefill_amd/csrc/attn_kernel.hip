@@ -299,7 +299,9 @@ __device__ inline float load_sink(const float* sink, int head) {
 
 // Q fragments as the MFMAs take them: zero for rows past the chunk; fp16 Q
 // pre-scaled by scale * log2 e (one fp16 rounding), so that S comes out of
-// the MFMA in exp2 units; bf16 Q as loaded.
+// the MFMA in exp2 units; bf16 Q as loaded.  The fp16 product is finite for
+// every fp16 q (|q| <= 65504) as long as |scale| * log2 e <= 1; the host
+// declines fp16 calls with a larger scale.
 template <typename TI, int KSTEPS>
 __device__ inline void prepare_q(u32x4* qf, float c, bool valid) {
 #pragma unroll

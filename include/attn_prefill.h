@@ -58,7 +58,9 @@
  *    buffers is touched and nothing is allocated.
  *  - Return codes: ATTN_OK; ATTN_DECLINED (-1): the request is valid but not
  *    supported (d not 64/128/256, dtype not f16/bf16, out dtype neither the input
- *    dtype nor f32, misaligned pointers, device not gfx950) -- nothing is
+ *    dtype nor f32, misaligned pointers, device not gfx950, fp16 inputs with
+ *    |scale| > ln 2: fp16 q is pre-scaled by scale * log2 e in fp16, which
+ *    stays finite for every fp16 q only up to that scale) -- nothing is
  *    launched and out is untouched, so the caller can fall back; ATTN_EINVAL
  *    (-2): invalid arguments (null pointers, non-positive sizes, h_q not a
  *    multiple of h_kv, past_len < 0, past_len + sq > s_cap, cu_seqlens not

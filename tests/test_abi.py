@@ -63,6 +63,8 @@ def _varlen(L, cu, past, *, window=-1, h_q=8, h_kv=2, d=64, s_cap=64, log=None, 
     (dict(dtype=3, out_dtype=3), binding.ATTN_DECLINED),  # f32 inputs
     (dict(dtype=1, out_dtype=2), binding.ATTN_DECLINED),  # f16 in, bf16 out
     (dict(q=MISALIGNED), binding.ATTN_DECLINED),
+    (dict(scale=0.7), binding.ATTN_DECLINED),             # fp16: q * scale * log2 e may overflow
+    (dict(scale=-0.7), binding.ATTN_DECLINED),
 ])
 def test_rejects_before_touching_a_device(L, kw, code):
     assert _call(L, **kw) == code
@@ -184,3 +186,10 @@ def test_noalloc_entry_checks_its_scratch_limit_before_any_gpu_call():
     assert "scratch" in binding.attn_last_error()
     assert call(0) == binding.ATTN_EINVAL
     assert call(2, h_q=6) == binding.ATTN_EINVAL   # h_q not a multiple of h_kv
+
+
+def test_scale_limit_names_the_reason(L):
+    # only requests that fail validation are made here: fake pointers never
+    # reach a device
+    assert _call(L, scale=0.7) == binding.ATTN_DECLINED
+    assert "scale" in binding.attn_last_error()
