@@ -21,7 +21,7 @@ ATTN_LOG_FIELDS = 40
 ATTN_LOG_MAX_WAVES = 8
 ATTN_LOG_WAVES = 16
 LOG_FIELDS = ("b", "h_first", "n_heads", "q_first", "q_last", "t_first", "t_last",
-              "n_visited", "n_waves", "n_splits", "part", "n_parts")
+              "n_visited", "n_waves", "n_splits", "part", "n_parts", "rows_per_wave")
 
 _DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
 

@@ -382,7 +382,8 @@ __device__ inline void finish_row(const Params& p, const f32x16* acc, float m_ru
 // the range from its offset w / R, so the waves of one offset visit runs of
 // one residue class: their union is counted by merging the R runs (sorted by
 // first tile), two runs joining when the gap between them is at most S.
-template <int R, int S>
+// Row group r covers Q-tile rows [r ROWS_PER_WAVE, (r + 1) ROWS_PER_WAVE).
+template <int R, int S, int ROWS_PER_WAVE = 32>
 __device__ void write_tile_log(const Params& p, void* lds_raw, int wave, int v_first, int v_last,
                                int v_count, int slot, int h_first, int q0, int q_last) {
   constexpr int NW = R * S;
@@ -450,7 +451,8 @@ __device__ void write_tile_log(const Params& p, void* lds_raw, int wave, int v_f
   rec[10] = blockIdx.y;
   rec[11] = gridDim.y;
 #pragma unroll
-  for (int i = 12; i < 16; ++i) rec[i] = 0;
+  for (int i = 13; i < 16; ++i) rec[i] = 0;
+  rec[12] = ROWS_PER_WAVE;
 #pragma unroll
   for (int w = 0; w < kLogMaxWaves; ++w) {
     rec[16 + 3 * w + 0] = w < NW ? wl[3 * w + 0] : -1;
@@ -1385,14 +1387,18 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Tile t is read by M_{t-2} (K fragments) and M_{t-1} (V fragments).  Its
-  // direct loads are issued in M_{t-NS+1} (the prologue for t < NS - 1) into
-  // the slot of tile t - NS, whose last reader M_{t-NS-1} finished before the
-  // barrier that opened V_{t-NS-1}.  The end of V_j waits for tile j + 3;
-  // later tiles may still be in flight.
+  // Tile t is read by M_{t-2} (K fragments) and M_{t-1} (V fragments; the
+  // reads are issued in M_{t-2}).  Its direct loads are issued in M_{t-NS}
+  // (the prologue for t < NS) into the slot of tile t - NS, whose last
+  // fragment reads were issued in M_{t-NS-1} and completed by every wave
+  // before the barrier that ends V_{t-NS-1} (each V phase ends with
+  // lgkmcnt(0)).  The end of V_j waits for tile j + 3; the tile after it may
+  // still be in flight, so each load has about two phases to land.  (Issuing
+  // K one tile earlier still, into the half of a slot that frees first, ran
+  // slower.)
   auto wait_tiles = [&](int j) {
-    const int newest = min(j + NS - 1, n_stages - 1);  // last tile requested so far
-    const int ahead = newest - (j + 3);                 // tiles allowed in flight
+    const int newest = min(j < 0 ? NS - 1 : j + NS, n_stages - 1);  // last tile requested
+    const int ahead = newest - (j + 3);  // tiles allowed in flight
     if (NS == 5 && ahead >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
     else if (ahead >= 1)
@@ -1401,34 +1407,36 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
 
-  // ---- prologue: tiles 0 .. NS-2 requested, 0 and 1 landed ----
+  // ---- prologue: tiles 0 .. NS-1 requested, 0 and 1 landed ----
   if (paged) {
     // the pool rows of the first tiles are read together, then each tile is
     // issued (one index round trip instead of one per tile)
-    uint32_t pre[NS - 1][LPW];
+    uint32_t pre[NS][LPW];
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
+    for (int j = 0; j < NS; ++j)
 #pragma unroll
       for (int i = 0; i < LPW; ++i) pre[j][i] = (uint32_t)kv_list[tile_key(j, i)];
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j) {
+    for (int j = 0; j < NS; ++j) {
       if (j >= n_stages) break;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) prow[i] = pre[j][i];
       load_tile(j);
     }
-    if (NS - 1 < n_stages) fetch_rows(NS - 1);
+    if (NS < n_stages) fetch_rows(NS);
   } else {
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
+    for (int j = 0; j < NS; ++j)
       if (j < n_stages) load_tile(j);
   }
   prepare_q<TI, KSTEPS>(qf, c, valid);
   {
-    const int newest = min(NS - 2, n_stages - 1);
-    if (newest - 1 >= 2 && NS == 5)
+    const int in_flight = min(NS - 1, n_stages - 1) - 1;  // tiles 2 .. newest
+    if (in_flight >= 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPW));
+    else if (in_flight == 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
-    else if (newest - 1 >= 1)
+    else if (in_flight == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1443,13 +1451,14 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     m_phase(j);
     // the direct loads go after the MFMAs: issued while the last ones drain
     __builtin_amdgcn_sched_barrier(0);
-    if (j >= 0 && j + NS - 1 < n_stages) load_tile(j + NS - 1);
-    if (paged && j >= 0 && j + NS < n_stages) fetch_rows(j + NS);
+    if (j >= 0 && j + NS < n_stages) load_tile(j + NS);
+    if (paged && j >= 0 && j + NS + 1 < n_stages) fetch_rows(j + NS + 1);
     __builtin_amdgcn_s_setprio(0);
     barrier();
     // ---- V_j ----
     v_phase(j);
     wait_tiles(j);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads done
     barrier();
   }
   // the last prefetch reads must be done before LDS is reused for the merge

@@ -101,12 +101,14 @@ enum {
   ATTN_LOG_N_VISITED = 7,/* distinct KV tiles some wave used                 */
   ATTN_LOG_N_WAVES = 8,  /* waves reported below (<= ATTN_LOG_MAX_WAVES)      */
   ATTN_LOG_N_SPLITS = 9, /* waves per row group: wave w serves Q-tile rows
-                            [32 (w % R), 32 (w % R) + 31], R = n_waves /
-                            n_splits, and takes the tiles t of its range with
+                            [W (w % R), W (w % R) + W - 1], W = rows per
+                            wave, R = n_waves / n_splits, and takes the tiles
+                            t of its range with
                             (t - range_first) % n_splits == w / R            */
   ATTN_LOG_PART = 10,    /* KV part of this record (attn_prefill_split)       */
   ATTN_LOG_N_PARTS = 11, /* KV parts per Q tile (n_split; 1 otherwise)       */
-  /* 12..15 reserved (0) */
+  ATTN_LOG_ROWS_PER_WAVE = 12, /* W above (32 or 64)                          */
+  /* 13..15 reserved (0) */
   ATTN_LOG_WAVES = 16,   /* wave w: fields 16 + 3w: first tile it used (-1:
                             none), + 1: last tile it used (-1: none), + 2: how
                             many tiles it used                               */

@@ -104,7 +104,8 @@ def check_tile_log(recs, bkv, q_rows, cu, past, window, h_q, causal=True):
     integer for integer.  Every compared number is an observation of the
     kernel: each wave notes the tiles whose scores its softmax used, and the
     record's union is formed from those notes.  Checks:
-      * each wave used exactly the tiles of its own residue class (it takes
+      * each wave (32 or 64 rows, as the record says) used exactly the tiles
+        of its own residue class (it takes
         every n_splits-th tile of its part of the range) that hold a key some
         row of the wave keeps (the oracle's range over the wave's rows);
       * each record's union is its part of the Q tile's range, the parts of a
@@ -125,7 +126,8 @@ def check_tile_log(recs, bkv, q_rows, cu, past, window, h_q, causal=True):
         skv = past[b] + sq
         assert 0 <= q0 <= q1 < sq and q1 - q0 + 1 <= q_rows and q0 % q_rows == 0, rec
         assert 1 <= nw <= binding.ATTN_LOG_MAX_WAVES and ns >= 1 and nw % ns == 0, rec
-        assert 0 <= part < nparts and rec[12:16] == [0, 0, 0, 0], rec
+        rpw = rec[12]
+        assert 0 <= part < nparts and rpw in (32, 64) and rec[13:16] == [0, 0, 0], rec
         lo, hi = _range(past[b], q0, q1, window, bkv, skv, causal)
         if nparts == 1:
             pl, ph = lo, hi
@@ -143,8 +145,8 @@ def check_tile_log(recs, bkv, q_rows, cu, past, window, h_q, causal=True):
                 assert got == (-1, -1, 0), (rec[:12], w, got)
                 continue
             rg, sp = w % n_rg, w // n_rg
-            wp0 = q0 + (rg * 32) // nh
-            wp1 = min(q0 + (rg * 32 + 31) // nh, sq - 1)
+            wp0 = q0 + (rg * rpw) // nh
+            wp1 = min(q0 + (rg * rpw + rpw - 1) // nh, sq - 1)
             if wp0 >= sq or ph < pl:
                 exp = (-1, -1, 0)
             else:
