@@ -155,13 +155,39 @@ def dist(xs, nd=3):
 
 
 def _load_lib(path):
-    """A library build's attn_prefill through ctypes (for A/B timing)."""
+    """A library build's attn_prefill / attn_prefill_varlen through ctypes
+    (for A/B timing)."""
     L = ctypes.CDLL(path)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    i32p = ctypes.POINTER(ctypes.c_int32)
     L.attn_prefill.argtypes = [vp, vp, vp, i32, i32, vp, ctypes.c_float, vp, i32, i32, i32, i32,
                                i32, i32, i32, vp]
     L.attn_prefill.restype = ctypes.c_int
+    L.attn_prefill_varlen.argtypes = [vp, vp, vp, i32p, i32p, i32, i32, vp, ctypes.c_float, vp,
+                                      i32, i32, i32, i32, i32, i32, vp, vp]
+    L.attn_prefill_varlen.restype = ctypes.c_int
     return L
+
+
+def ragged_calls(torch, binding, reps=8):
+    """`reps` calls of the ragged bf16 d 128 batch (8 sequences, 16 q / 2 KV
+    heads, window 128, bf16 out) as attn_prefill_varlen argument tuples."""
+    from gqa_flash_attention_prefill_amd import synth
+    rc = synth.ragged_bf16()
+    rc = synth.Case(rc.name, h_q=rc.h_q, h_kv=rc.h_kv, d=rc.d, sq=list(rc.sq), past=list(rc.past),
+                    window=rc.window, dtype=rc.dtype, seed=rc.seed, poison_tail=False)
+    inp = synth.make(rc, device="cuda:0")
+    out = torch.empty_like(inp["q"])
+    batch, h_kv, s_cap, d = inp["k_cache"].shape
+    cu, past = inp["cu_seqlens"], inp["past_len"]
+    keep = (inp, out)
+    a = (ctypes.c_void_p(inp["q"].data_ptr()), ctypes.c_void_p(inp["k_cache"].data_ptr()),
+         ctypes.c_void_p(inp["v_cache"].data_ptr()), (ctypes.c_int32 * len(cu))(*cu),
+         (ctypes.c_int32 * len(past))(*past), len(past), rc.window,
+         ctypes.c_void_p(inp["sink"].data_ptr()), ctypes.c_float(rc.scale),
+         ctypes.c_void_p(out.data_ptr()), rc.h_q, h_kv, d, s_cap, binding.ATTN_BF16,
+         binding.ATTN_BF16, None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    return [("attn_prefill_varlen", keep, a)] * reps
 
 
 def ab_compare(torch, binding, lib_b, rounds, layers_calls):
@@ -173,9 +199,10 @@ def ab_compare(torch, binding, lib_b, rounds, layers_calls):
     stream = torch.cuda.current_stream()
 
     def step(L):
-        for _, _, a in layers_calls:
-            if L.attn_prefill(*a) != 0:
-                raise RuntimeError("attn_prefill failed in the A/B run")
+        for fn, _, a in layers_calls:
+            f = getattr(L, fn) if isinstance(fn, str) else L.attn_prefill
+            if f(*a) != 0:
+                raise RuntimeError("attention call failed in the A/B run")
 
     for L in (A, B):
         step(L)
@@ -704,8 +731,9 @@ def main():
     ap.add_argument("--ab", default=None, metavar="LIB_B",
                     help="interleaved A/B/A timing of the in-tree library against another build")
     ap.add_argument("--ab-rounds", type=int, default=10)
-    ap.add_argument("--ab-kind", choices=("all", "full", "window"), default="all",
-                    help="A/B over every call of the step, or only one layer type's calls")
+    ap.add_argument("--ab-kind", choices=("all", "full", "window", "ragged"), default="all",
+                    help="A/B over every call of the step, only one layer type's calls, or "
+                         "8 calls of the ragged bf16 d 128 batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-demo", action="store_true",
                     help="time a 64-sequence decode step (prints its own JSON line)")
@@ -819,8 +847,11 @@ def main():
     sweeps = binding.attn_tune_stats()
 
     if args.ab:
-        keep = {"all": lambda w: True, "full": lambda w: w <= 0, "window": lambda w: w > 0}
-        sel = [cl for cl in calls if keep[args.ab_kind](layer_window(cl[0]))]
+        if args.ab_kind == "ragged":
+            sel = ragged_calls(torch, binding)
+        else:
+            keep = {"all": lambda w: True, "full": lambda w: w <= 0, "window": lambda w: w > 0}
+            sel = [cl for cl in calls if keep[args.ab_kind](layer_window(cl[0]))]
         res = ab_compare(torch, binding, args.ab, args.ab_rounds, sel)
         res["calls"] = f"{args.ab_kind} ({len(sel)} calls per step)"
         print(json.dumps(res), flush=True)

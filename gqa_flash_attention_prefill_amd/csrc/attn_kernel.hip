@@ -223,6 +223,12 @@ __device__ inline uint32_t lds_byte_addr(const void* p) {
 constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | (15 << 8) | (7 << 4) | (n & 15); }
 __device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Helpers that take the kernel arguments (Params) by reference, and the
+// kernels' lambdas (which capture them by reference), are always inlined: a
+// call that is not needs the arguments' address, and the compiler then
+// copies the whole 2.5 KB argument block into per-lane scratch at kernel
+// entry (it did so for the d 128 and d 256 instantiations).
+//
 // One workgroup's work item: KV head g, head group hg and Q tile of sequence
 // bi (items run heaviest Q tile first).  The first sequence's table entries
 // are read together with the scalars the item depends on, so a one-sequence
@@ -233,7 +239,7 @@ struct WorkItem {
   int64_t tok0;
 };
 template <bool XTRA, bool BATCH>
-__device__ inline WorkItem decode_item(const Params& p, int item) {
+__device__ __attribute__((always_inline)) WorkItem decode_item(const Params& p, int item) {
   int n_seq = p.seq.n_seq, n_tiles = p.seq.n_tiles;
   int h_kv = p.h_kv, n_hg = p.n_hgroups, q_rows = p.q_rows;
   int cu0 = p.seq.cu_q[0], cu1 = p.seq.cu_q[1], tile0 = 0;
@@ -329,7 +335,8 @@ __device__ inline void prepare_q(u32x4* qf, float c, bool valid) {
 //     acc / l_kept in fp32 and m + log2 l_kept (log2 units), or 0 and -inf
 //     when this part of the KV range kept no key of the row.
 template <int D, bool XTRA, typename TI, typename TO>
-__device__ inline void finish_row(const Params& p, const f32x16* acc, float m_run, float l_kept,
+__device__ __attribute__((always_inline)) void finish_row(const Params& p, const f32x16* acc,
+                                                          float m_run, float l_kept,
                                   float sink, int64_t tok, int head, int half) {
   constexpr int DB = D / 32;
   const float kNegInf = -__builtin_inff();
@@ -384,7 +391,8 @@ __device__ inline void finish_row(const Params& p, const f32x16* acc, float m_ru
 // first tile), two runs joining when the gap between them is at most S.
 // Row group r covers Q-tile rows [r ROWS_PER_WAVE, (r + 1) ROWS_PER_WAVE).
 template <int R, int S, int ROWS_PER_WAVE = 32>
-__device__ void write_tile_log(const Params& p, void* lds_raw, int wave, int v_first, int v_last,
+__device__ __attribute__((always_inline)) void write_tile_log(const Params& p, void* lds_raw,
+                                                              int wave, int v_first, int v_last,
                                int v_count, int slot, int h_first, int q0, int q_last) {
   constexpr int NW = R * S;
   static_assert(NW <= kLogMaxWaves, "record holds every wave");
@@ -463,7 +471,7 @@ __device__ void write_tile_log(const Params& p, void* lds_raw, int wave, int v_f
 
 // This workgroup's part of the Q tile's KV tiles [t_lo, t_hi] when the range
 // is cut into p.n_split contiguous parts (blockIdx.y); may come out empty.
-__device__ inline void split_range(const Params& p, int* t_lo, int* t_hi) {
+__device__ __attribute__((always_inline)) void split_range(const Params& p, int* t_lo, int* t_hi) {
   if (p.n_split <= 1) return;
   const int per = (*t_hi - *t_lo + p.n_split) / p.n_split;  // ceil(tiles / n_split)
   const int lo = *t_lo + (int)blockIdx.y * per;
@@ -628,23 +636,23 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   const uint32_t lds_addr = lds_byte_addr(lds);
   // Each step loads this wave's pieces of a stage's K / V tile-tensors:
   // K pieces of stage kst, V pieces of stage vst (a negative stage: none).
-  auto piece_is_v = [&](int i) { return (((wave * LD_PER_WAVE + i) / (TILE_CH / 64)) & 1) != 0; };
-  auto piece_stage = [&](int i, int kst, int vst) { return piece_is_v(i) ? vst : kst; };
+  auto piece_is_v = [&](int i) __attribute__((always_inline)) { return (((wave * LD_PER_WAVE + i) / (TILE_CH / 64)) & 1) != 0; };
+  auto piece_stage = [&](int i, int kst, int vst) __attribute__((always_inline)) { return piece_is_v(i) ? vst : kst; };
   // Token-pool layout: the pool row of each of this lane's keys in the next
   // loads, read one step ahead so that the index latency hides behind the
   // step before it (keys past the sequence read row skv - 1).
   uint32_t prow[LD_PER_WAVE];
-  auto piece_key = [&](int i, int stage) {
+  auto piece_key = [&](int i, int stage) __attribute__((always_inline)) {
     const int tt = (wave * LD_PER_WAVE + i) / (TILE_CH / 64);
     const int t = min(t_lo + max(stage, 0) * S + (tt >> 1), t_hi);
     return min(t * BKV + ld_key[i], skv - 1);
   };
-  auto fetch_rows = [&](int kst, int vst) {
+  auto fetch_rows = [&](int kst, int vst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LD_PER_WAVE; ++i)
       prow[i] = (uint32_t)kv_list[piece_key(i, piece_stage(i, kst, vst))];
   };
-  auto load_kv = [&](int kst, int vst) {
+  auto load_kv = [&](int kst, int vst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LD_PER_WAVE; ++i) {
       const int qi = wave * LD_PER_WAVE + i;
@@ -676,10 +684,10 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   };
   // does this wave issue any piece for (kst, vst)?  (its pieces are of one
   // tensor whenever the answer decides a wait)
-  auto issues = [&](int kst, int vst) { return piece_is_v(0) ? vst >= 0 : kst >= 0; };
+  auto issues = [&](int kst, int vst) __attribute__((always_inline)) { return piece_is_v(0) ? vst >= 0 : kst >= 0; };
   // wait until every load but this step's newest ones has landed in LDS
   // (`newest`: whether this wave issued loads in this step)
-  auto wait_older = [&](bool newest) {
+  auto wait_older = [&](bool newest) __attribute__((always_inline)) {
     if (NSLOT == 4 && newest)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(LD_PER_WAVE));
     else
@@ -699,13 +707,13 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   f32x16 negm = f32x16{}; // splat(-m_use): MFMA accumulator input (prescaled-Q path)
 
   // tile this wave handles at stage j (if any)
-  auto wave_tile = [&](int j, int* t) {
+  auto wave_tile = [&](int j, int* t) __attribute__((always_inline)) {
     *t = t_lo + j * S + sp;
     return wave_live && j < n_stages && *t <= t_hi && *t >= w_lo && *t <= w_hi;
   };
 
   // S^T of tile t from stage slot `st`, in exp2 units relative to m_use, masked
-  auto scores = [&](const u32x4* kt, int t, f32x16* sc) {
+  auto scores = [&](const u32x4* kt, int t, f32x16* sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int kr = nb * 32 + col;
@@ -719,7 +727,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
     }
   };
   // bf16 path: scores to exp2 units relative to m_use (fp16 path: already)
-  auto to_exp2_units = [&](f32x16* sc) {
+  auto to_exp2_units = [&](f32x16* sc) __attribute__((always_inline)) {
     if constexpr (!TI::kPrescaleQ) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -729,7 +737,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   };
   // row max of a tile (v_maximum3_f32 tree; IEEE maximum needs no NaN
   // canonicalisation), combined over the two lane halves
-  auto row_max = [&](const f32x16* sc) {
+  auto row_max = [&](const f32x16* sc) __attribute__((always_inline)) {
     float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -739,11 +747,11 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
     return pair_max(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])));
   };
   // is tile t free of masked (row, key) pairs for every row of this wave?
-  auto interior = [&](int t) {
+  auto interior = [&](int t) __attribute__((always_inline)) {
     const int kbase = t * BKV;
     return (kbase + BKV - 1 <= w_full_hi) && (kbase >= w_full_lo);
   };
-  auto apply_mask = [&](int t, f32x16* sc) {
+  auto apply_mask = [&](int t, f32x16* sc) __attribute__((always_inline)) {
     const int kbase = t * BKV;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -754,12 +762,12 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
       }
   };
   // masked, exp2-unit scores and their row max
-  auto prepare = [&](int t, f32x16* sc) {
+  auto prepare = [&](int t, f32x16* sc) __attribute__((always_inline)) {
     to_exp2_units(sc);
     if (!interior(t)) apply_mask(t, sc);
     return row_max(sc);
   };
-  auto set_neg_inf = [&](f32x16* sc) {
+  auto set_neg_inf = [&](f32x16* sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -767,7 +775,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   };
   // raise the reference max if the tile needs it (wave-uniform branch);
   // acc must not have pending PV work of an older tile when this runs
-  auto rebase = [&](float mx, f32x16* sc) {
+  auto rebase = [&](float mx, f32x16* sc) __attribute__((always_inline)) {
     const bool need = (mx > kRescale) || (m_run == kNegInf && mx != kNegInf);
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float mx_abs = mx + m_use;  // -inf stays -inf
@@ -792,7 +800,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   // The tiles whose scores this wave actually uses (visited-tile record):
   // noted where the softmax consumes a tile, not derived from the bounds.
   int v_first = -1, v_last = -1, v_count = 0;
-  auto note = [&](int t) {
+  auto note = [&](int t) __attribute__((always_inline)) {
     if (v_count == 0) v_first = t;
     v_last = t;
     ++v_count;
@@ -801,8 +809,8 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   // ---- prologue: K of stages 0 .. KD-1 and V of stages 0 .. KD-2 (the
   // first K and V always, later ones if the stage exists); then every one
   // but the last step's is resident, and S of the wave's first tile ----
-  auto pro_k = [&](int s2) { return (s2 == 0 || s2 < n_stages) ? s2 : -1; };
-  auto pro_v = [&](int s2) { return (s2 == 1 || (s2 >= 1 && s2 - 1 < n_stages)) ? s2 - 1 : -1; };
+  auto pro_k = [&](int s2) __attribute__((always_inline)) { return (s2 == 0 || s2 < n_stages) ? s2 : -1; };
+  auto pro_v = [&](int s2) __attribute__((always_inline)) { return (s2 == 1 || (s2 >= 1 && s2 - 1 < n_stages)) ? s2 - 1 : -1; };
   if (paged) {
     // the pool rows of the first steps are read together, then each step's
     // loads are issued (one index round trip instead of one per step)
@@ -839,7 +847,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
   }
 
   // P = exp2(S) of the current tile, 16-bit; returns this lane's row sum
-  auto make_p = [&](const f32x16* s_cur, u32x4* pb, u32x4* pl) {
+  auto make_p = [&](const f32x16* s_cur, u32x4* pb, u32x4* pl) __attribute__((always_inline)) {
     float rs = 0.f;
 #pragma unroll
     for (int g16 = 0; g16 < NG; ++g16)
@@ -859,7 +867,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
       }
     return rs;
   };
-  auto pv = [&](const u32x4* vt, const u32x4* pb, const u32x4* pl) {
+  auto pv = [&](const u32x4* vt, const u32x4* pb, const u32x4* pl) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -870,7 +878,7 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
       }
   };
 
-  auto stage_step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
+  auto stage_step = [&](int j, f32x16* s_cur, f32x16* s_nxt) __attribute__((always_inline)) {
     // K of stage j + KD (first read by step j + KD - 1) and V of stage
     // j + KD - 1 (read by that same step); their slots' last readers were
     // steps j - 1 (K) and j - 1 (V)
@@ -1089,15 +1097,15 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // tile to load, read one tile ahead so that the index latency hides behind
   // the phases before it (keys past the sequence read row skv - 1).
   uint32_t prow[LPW];
-  auto tile_key = [&](int j, int i) {
+  auto tile_key = [&](int j, int i) __attribute__((always_inline)) {
     const int t = min(t_lo + 2 * j + grp, t_hi);
     return min(t * BKV + ld_key[i], skv - 1);
   };
-  auto fetch_rows = [&](int j) {
+  auto fetch_rows = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) prow[i] = (uint32_t)kv_list[tile_key(j, i)];
   };
-  auto load_tile = [&](int j) {
+  auto load_tile = [&](int j) __attribute__((always_inline)) {
     const int t = min(t_lo + 2 * j + grp, t_hi);
     const uint32_t st = ring_addr + (uint32_t)((j % NS) * SLOT_CH) * 16u;
     const bool tail = t * BKV + BKV > skv;  // the tile that crosses the end of the keys
@@ -1123,7 +1131,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     }
   };
 
-  auto wave_tile = [&](int j, int* t) {
+  auto wave_tile = [&](int j, int* t) __attribute__((always_inline)) {
     *t = t_lo + 2 * j + grp;
     return wave_live && j >= 0 && j < n_stages && *t <= t_hi && *t >= w_lo && *t <= w_hi;
   };
@@ -1151,6 +1159,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   u32x4 vf[DB][NG];
   u32x4 pb[NG], pl[NG];
   u32x4 psum = {0, 0, 0, 0};  // fp16: the tile's P pre-added (see presum)
+  float l_vec = 0.f;          // fp16: this lane's part of the row sum
   bool started = false;       // wave-uniform: every row holds a reference max
 #pragma unroll
   for (int g16 = 0; g16 < NG; ++g16) {
@@ -1160,7 +1169,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     for (int db = 0; db < DB; ++db) vf[db][g16] = u32x4{0, 0, 0, 0};
   }
 
-  auto read_k = [&](int j) {
+  auto read_k = [&](int j) __attribute__((always_inline)) {
     const u32x4* kt = ring + (j % NS) * SLOT_CH;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -1170,7 +1179,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         kf[nb][kk] = kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)];
       }
   };
-  auto read_v = [&](int j) {
+  auto read_v = [&](int j) __attribute__((always_inline)) {
     const u32x4* vt = ring + (j % NS) * SLOT_CH + TILE_CH;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -1185,12 +1194,12 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // wave's issue slots busy while the matrix pipe runs, without the read
   // bursts that overflow the LDS command queue (four waves of a CU are in
   // this phase at once).
-  auto m_phase = [&](int j) {
+  auto m_phase = [&](int j) __attribute__((always_inline)) {
     const u32x4* kt = ring + ((j + 2) % NS) * SLOT_CH;
     const u32x4* vt = ring + ((j + 1) % NS) * SLOT_CH + TILE_CH;
     constexpr int kMfma = 0x008, kDsRead = 0x100;
     constexpr int PVM = TI::kSplitP ? 2 : 1;   // MFMAs per P.V step
-    auto refill_k = [&](int i) {
+    auto refill_k = [&](int i) __attribute__((always_inline)) {
       const int kk = i / NB, nb = i % NB;
       const int kr = nb * 32 + col;
       kf[nb][kk] = kt[kr * DCH + k_chunk<D>(kr, 2 * kk + half)];
@@ -1216,9 +1225,6 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       if constexpr (TI::kSplitP) {
         lsum = TI::mma(ones, pb[g16], lsum);
         lsum = TI::mma(ones, pl[g16], lsum);
-      } else if (g16 == NG - 1) {
-        // fp16: one row-sum MFMA for the tile over its pre-added P
-        lsum = TI::mma(ones, psum, lsum);
       }
       vf[DB - 1][g16] = v_frag<D>(vt, g16, DB - 1, lane);
     }
@@ -1238,11 +1244,11 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         if (g16 == 0 && db == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
         else if (db > 0) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
       }
-      if (TI::kSplitP || g16 == NG - 1) __builtin_amdgcn_sched_group_barrier(kMfma, PVM, 0);
+      if (TI::kSplitP) __builtin_amdgcn_sched_group_barrier(kMfma, PVM, 0);
       __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
     }
   };
-  auto make_p = [&]() {
+  auto make_p = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int g16 = 0; g16 < NG; ++g16)
 #pragma unroll
@@ -1257,7 +1263,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       }
   };
   // in-lane part of the row max (the other 16 keys of each row are in lane ^ 32)
-  auto lane_max = [&]() {
+  auto lane_max = [&]() __attribute__((always_inline)) {
     float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -1266,7 +1272,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[nb][i], sc[nb][i + 1]));
     return vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]));
   };
-  auto apply_mask = [&](int t) {
+  auto apply_mask = [&](int t) __attribute__((always_inline)) {
     const int kbase = t * BKV;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -1279,7 +1285,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
 
   // The tiles whose scores this wave actually uses (visited-tile record)
   int v_first = -1, v_last = -1, v_count = 0;
-  auto note = [&](int t) {
+  auto note = [&](int t) __attribute__((always_inline)) {
     if (v_count == 0) v_first = t;
     v_last = t;
     ++v_count;
@@ -1291,7 +1297,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // O and l rescaled and P formed again.
   // fp16: the tile's four 16-key P vectors added as packed fp16 (whole-vector
   // adds), the operand of the tile's one row-sum MFMA in the next M phase
-  auto presum = [&]() {
+  auto presum = [&]() __attribute__((always_inline)) {
     if constexpr (!TI::kSplitP) {
       f16x8 sum = __builtin_bit_cast(f16x8, pb[0]);
 #pragma unroll
@@ -1302,11 +1308,12 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // Raise the reference max to the tile's row max where it exceeds it by more
   // than kRescale (or where the row had none), rescaling O and l, then form P
   // again; `mx` is the row max of S relative to the current reference.
-  auto rescale = [&](float mx) {
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
     const float mx_abs = mx + m_use;
     const float m_new = fmaxf(m_run, mx_abs);
     const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     lsum *= alpha;
+    l_vec *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     m_run = m_new;
@@ -1324,7 +1331,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   };
   // Does some element of the pre-added P exceed 2^10 (or is it inf / NaN)?
   // Non-negative fp16 values order as their bit patterns.
-  auto psum_big = [&]() {
+  auto psum_big = [&]() __attribute__((always_inline)) {
     u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, psum[0]),
                                         __builtin_bit_cast(u16x2, psum[1]));
     const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, psum[2]),
@@ -1342,7 +1349,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   //  * otherwise (boundary tiles, a wave's first tiles, bf16): mask, the row
   //    max over both lane halves, and a raise of the reference when some
   //    row's max exceeds it by more than kRescale or a row had none.
-  auto v_phase = [&](int j) {
+  auto v_phase = [&](int j) __attribute__((always_inline)) {
     int t = 0;
     const bool ok = wave_tile(j + 1, &t);
     if (ok) {
@@ -1369,6 +1376,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         rescale(mx);
         presum();
       }
+      if constexpr (!TI::kSplitP) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l_vec = TI::rowsum(psum[e], l_vec);
+      }
       if (!fast) started = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
     } else {
 #pragma unroll
@@ -1379,7 +1390,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       psum = u32x4{0, 0, 0, 0};
     }
   };
-  auto barrier = [&]() {
+  auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -1396,7 +1407,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // still be in flight, so each load has about two phases to land.  (Issuing
   // K one tile earlier still, into the half of a slot that frees first, ran
   // slower.)
-  auto wait_tiles = [&](int j) {
+  auto wait_tiles = [&](int j) __attribute__((always_inline)) {
     const int newest = min(j < 0 ? NS - 1 : j + NS, n_stages - 1);  // last tile requested
     const int ahead = newest - (j + 3);  // tiles allowed in flight
     if (NS == 5 && ahead >= 2)
@@ -1465,7 +1476,8 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   if (grp == 0) barrier();
 
-  float l_run = lsum[0];  // the row's full sum (both lane halves' keys)
+  // the row's full sum (both lane halves' keys)
+  float l_run = TI::kSplitP ? lsum[0] : l_vec + other_half(l_vec);
   // ---- merge the two groups' partial (m, l, O) through LDS ----
   {
     constexpr int NV = 2 + 16 * DB;
