@@ -250,28 +250,65 @@ int sweep(const Call& c_in, int* best_out) {
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
     return fail(ATTN_EHIP, "hipEventCreate failed");
-  const int reps = 3;
-  float best_ms = INFINITY;
-  int best = 0;
+  // Three passes over the configurations (interleaved, so that a drift of
+  // the clock hits all of them alike); in each, a configuration is launched
+  // back to back until at least kMinBatchUs of work is timed, and it is
+  // ranked by the median of its three per-call times.  Short calls (window
+  // chunks, decode rows) then get tens of repetitions per pass, and one slow
+  // or fast outlier pass does not decide the choice.
+  constexpr float kMinBatchUs = 150.f;
+  constexpr int kPasses = 3;
+  const int n_cfg = attn::config_count();
+  std::vector<float> pass_us(n_cfg * kPasses, INFINITY);
+  std::vector<int> reps(n_cfg, 3);
   int64_t launches = 0;
   int rc = ATTN_OK;
-  for (int i = 0; i < attn::config_count() && rc == ATTN_OK; ++i) {
-    rc = run_config(c, i, false, nullptr, nullptr);  // warm-up
-    ++launches;
-    if (rc) break;
-    if (hipEventRecord(e0, c.stream) != hipSuccess) { rc = fail(ATTN_EHIP, "event"); break; }
-    for (int r = 0; r < reps && rc == ATTN_OK; ++r, ++launches)
-      rc = run_config(c, i, false, nullptr, nullptr);
-    if (rc) break;
-    if (hipEventRecord(e1, c.stream) != hipSuccess) { rc = fail(ATTN_EHIP, "event"); break; }
-    if (hipEventSynchronize(e1) != hipSuccess) { rc = fail(ATTN_EHIP, "sweep sync"); break; }
+  auto timed = [&](int i, int n, float* us) {
+    if (hipEventRecord(e0, c.stream) != hipSuccess) return fail(ATTN_EHIP, "event");
+    for (int r = 0; r < n; ++r, ++launches) {
+      int rr = run_config(c, i, false, nullptr, nullptr);
+      if (rr) return rr;
+    }
+    if (hipEventRecord(e1, c.stream) != hipSuccess) return fail(ATTN_EHIP, "event");
+    if (hipEventSynchronize(e1) != hipSuccess) return fail(ATTN_EHIP, "sweep sync");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) { rc = fail(ATTN_EHIP, "event"); break; }
-    if (getenv("ATTN_PREFILL_TUNE_DEBUG"))
-      fprintf(stderr, "[attn_prefill tune] %-14s %9.3f us\n", attn::config(i).name,
-              1000.f * ms / reps);
-    if (ms < best_ms) { best_ms = ms; best = i; }
+    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return fail(ATTN_EHIP, "event");
+    *us = 1000.f * ms / n;
+    return (int)ATTN_OK;
+  };
+  for (int pass = 0; pass < kPasses && rc == ATTN_OK; ++pass) {
+    for (int i = 0; i < n_cfg && rc == ATTN_OK; ++i) {
+      float us = 0.f;
+      if (pass == 0) {
+        rc = run_config(c, i, false, nullptr, nullptr);  // warm-up
+        ++launches;
+        if (rc) break;
+        rc = timed(i, reps[i], &us);
+        if (rc) break;
+        if (us * reps[i] < kMinBatchUs) {
+          reps[i] = std::min(64, (int)std::ceil(kMinBatchUs / std::max(us, 0.5f)));
+          rc = timed(i, reps[i], &us);
+          if (rc) break;
+        }
+      } else {
+        rc = timed(i, reps[i], &us);
+        if (rc) break;
+      }
+      pass_us[i * kPasses + pass] = us;
+      if (getenv("ATTN_PREFILL_TUNE_DEBUG"))
+        fprintf(stderr, "[attn_prefill tune] %-20s pass %d %9.3f us (%d reps)\n",
+                attn::config(i).name, pass, us, reps[i]);
+    }
   }
+  auto median = [&](int i) {
+    float v[kPasses];
+    for (int k = 0; k < kPasses; ++k) v[k] = pass_us[i * kPasses + k];
+    std::sort(v, v + kPasses);
+    return v[kPasses / 2];
+  };
+  int best = 0;
+  for (int i = 1; i < n_cfg; ++i)
+    if (median(i) < median(best)) best = i;
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   g_tune_launches += launches;

@@ -279,9 +279,11 @@ const char* attn_last_error(void);
  * (d, sq, H_q, G) rather than the growing KV length, plus the window, which
  * caps the tiles a block walks).  Here the key is (d, dtype, out dtype, q
  * tokens of the call, h_q, group size, window, batch).  The first call for a
- * key times every kernel configuration once (a synchronous sweep on the
- * caller's stream, without the sink) and keeps the fastest; later calls with
- * the same key reuse it.  Since the key leaves out the KV depth, the sweep
+ * key times every kernel configuration (a synchronous sweep on the caller's
+ * stream, without the sink: three interleaved passes, each timing a
+ * configuration over at least ~150 us of back-to-back launches, ranked by
+ * the median) and keeps the fastest; later calls with the same key reuse
+ * it.  Since the key leaves out the KV depth, the sweep
  * times every sequence at depth max(past_len, min(s_cap, 16384) - sq) of the
  * caller's cache (see "The tuning sweep" above), so that the choice made on a
  * shallow first chunk holds for the deep ones.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and uses the

@@ -37,8 +37,10 @@ def test_one_sweep_per_layer_type_over_a_chunked_prefill(monkeypatch):
     n_cfg = binding.attn_config_count()
     assert st["sweeps"] == 2, st
     assert st["cached_keys"] == 2, st
-    # each sweep times every configuration: one warm-up and three timed launches
-    assert st["tuning_launches"] == 2 * n_cfg * 4, st
+    # each sweep times every configuration in three passes: a warm-up, a
+    # first batch of three launches, a longer batch (at most 64) when three
+    # take under ~150 us, and two more passes of the same length
+    assert 2 * n_cfg * 10 <= st["tuning_launches"] <= 2 * n_cfg * (1 + 3 + 3 * 64), st
     for _, _, out in layers:
         assert torch.isfinite(out).all()
     # the cache answers for exactly the two swept keys
