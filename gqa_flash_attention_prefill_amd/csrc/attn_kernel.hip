@@ -1330,12 +1330,15 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     make_p();
   };
   // Does some element of the pre-added P exceed 2^10 (or is it inf / NaN)?
-  // Non-negative fp16 values order as their bit patterns.
+  // Non-negative fp16 values order as their bit patterns.  The four words
+  // are copied out first: hipcc lowers a __builtin_bit_cast of a vector
+  // element (psum[i] directly) to a load of element 0 whatever i is.
   auto psum_big = [&]() __attribute__((always_inline)) {
-    u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, psum[0]),
-                                        __builtin_bit_cast(u16x2, psum[1]));
-    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, psum[2]),
-                                              __builtin_bit_cast(u16x2, psum[3]));
+    const uint32_t w0 = psum[0], w1 = psum[1], w2 = psum[2], w3 = psum[3];
+    u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w0),
+                                        __builtin_bit_cast(u16x2, w1));
+    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w2),
+                                              __builtin_bit_cast(u16x2, w3));
     a = __builtin_elementwise_max(a, b);
     return a[0] > kPsumMax || a[1] > kPsumMax;
   };

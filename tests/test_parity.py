@@ -150,6 +150,35 @@ def test_chunk_rows_match_whole_prefill_rows_bitwise():
             assert torch.equal(part, whole[c0:c0 + 128]), (cfg, c0)
 
 
+@pytest.mark.parametrize("residues", [(2, 3, 6, 7), (2,), (7,), (0, 1, 4, 5)])
+def test_scores_rising_far_past_the_reference(residues):
+    # Online softmax with a lazily raised reference max (FlashAttention-2,
+    # "Algorithm"; a stale max is exact after rescaling): a wave's first
+    # tiles set the reference near 0, then keys whose key index mod 8 is in
+    # `residues` score about 40 (log2 units) above it.  exp2 of that against
+    # the old reference overflows fp16, so the kernels must see the rise
+    # wherever the key sits in the tile and raise the reference before P is
+    # used; the result must stay finite and match the oracle.
+    case = synth.Case("rising", h_q=8, h_kv=2, d=64, sq=[128], past=[1024], window=-1,
+                      seed=31, poison_tail=False)
+    inp = synth.make(case)
+    q, k = inp["q"].float(), inp["k_cache"].float()
+    q = 1.0 + 0.05 * q                     # every row points along (1, ..., 1)
+    k = 0.05 * k                           # scores near 0 ...
+    keys = torch.arange(k.shape[2])
+    big = (keys >= 384) & (keys < 640) & torch.isin(keys % 8, torch.tensor(residues))
+    k[:, :, big, :] += 3.5                 # ... except these: q.k/8 * log2(e) ~ 40
+    inp["q"], inp["k_cache"] = q.half(), k.half()
+    ref = oracle_full(inp)
+    dev = to_device(inp)
+    for cfg in _each_config():
+        name = f"rising{residues}[{binding.attn_config_name(cfg)}]"
+        out, _, _, _ = run_gpu(dev, out_dtype=torch.float32)
+        got = f64(out)
+        assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+        check_rows(got, ref, name)
+
+
 def test_declined_request_leaves_output_untouched():
     q = torch.randn(16, 4, 96, device="cuda", dtype=torch.float16)
     k = torch.randn(1, 2, 16, 96, device="cuda", dtype=torch.float16)
