@@ -1135,6 +1135,12 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     *t = t_lo + 2 * j + grp;
     return wave_live && j >= 0 && j < n_stages && *t <= t_hi && *t >= w_lo && *t <= w_hi;
   };
+  // The tiles this wave visits that are interior (every key visible to every
+  // row of the wave) form one run tf_lo .. tf_hi of tile indices (empty when
+  // tf_hi < tf_lo); wave_tile holds on each of this group's tiles in it
+  // (t_lo + grp <= t <= t_hi puts the stage in range).
+  const int tf_lo = max(max(t_lo + grp, w_lo), (w_full_lo + BKV - 1) / BKV);
+  const int tf_hi = min(min(t_hi, w_hi), (w_full_hi + 1) / BKV - 1);
 
   float m_run = kNegInf, m_use = 0.f;
   // splat(-m_use), the accumulator input of the first S MFMA of each 32-key
@@ -1142,13 +1148,13 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // input in place would otherwise make the compiler copy it every phase
   f32x16 negm = f32x16{};
   f32x16 negm1 = f32x16{};
-  // Row sums of P on the matrix pipe: ones . P^T puts the sum of P over the
-  // tile's keys in every element of the row's column (the vector pipe is the
-  // busier one at d = 64).  fp16 inputs: the tile's four 16-key P vectors are
-  // first added as packed fp16 in the V phase (no sum exceeds 2^10: the V
-  // phase raises the reference max otherwise; one rounding of 2^-11 relative
-  // per add), then one MFMA sums them; bf16 inputs: one MFMA per 16-key step
-  // for each of P's two parts.
+  // Row sums of P.  fp16 inputs: the tile's four 16-key P vectors are added
+  // as packed fp16 in the V phase (no sum exceeds 2^10: the V phase raises
+  // the reference max otherwise; one rounding of 2^-11 relative per add) and
+  // the four pre-added words are summed into l_vec with v_dot2c.  bf16
+  // inputs: on the matrix pipe, where ones . P^T puts the sum of P over the
+  // tile's keys in every element of the row's column, one MFMA per 16-key
+  // step for each of P's two parts.
   f32x16 lsum = f32x16{};
   const u32x4 ones = {TI::kOnePair, TI::kOnePair, TI::kOnePair, TI::kOnePair};
   f32x16 acc[DB];
@@ -1343,39 +1349,27 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     return a[0] > kPsumMax || a[1] > kPsumMax;
   };
 
-  // One V phase: softmax of S_{j+1} into P_{j+1}.
-  //  * fp16, interior tile (no pair masked), every row of the wave already
-  //    holding a reference max: P is formed at once against that reference,
-  //    and the reference is raised only if some pre-added P exceeds 2^10
-  //    (then each p <= 2^10 otherwise, so the fp16 P and its pre-added sums
-  //    stay finite).  No row max is taken on this path.
-  //  * otherwise (boundary tiles, a wave's first tiles, bf16): mask, the row
-  //    max over both lane halves, and a raise of the reference when some
-  //    row's max exceeds it by more than kRescale or a row had none.
+  // One V phase: softmax of S_{j+1} into P_{j+1} (the general path: boundary
+  // tiles, a wave's first tiles, bf16, and iterations outside the steady
+  // run): mask, the row max over both lane halves, and a raise of the
+  // reference when some row's max exceeds it by more than kRescale or a row
+  // had none.
   auto v_phase = [&](int j) __attribute__((always_inline)) {
     int t = 0;
-    const bool ok = wave_tile(j + 1, &t);
-    if (ok) {
+    if (wave_tile(j + 1, &t)) {
       note(t);
       const bool inner = (t * BKV + BKV - 1 <= w_full_hi) && (t * BKV >= w_full_lo);
-      const bool fast = TI::kPrescaleQ && started && inner;
       if constexpr (!TI::kPrescaleQ) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[nb][i] = __builtin_fmaf(sc[nb][i], c, -m_use);
       }
-      float mx = 0.f;
-      if (!fast) {
-        if (!inner) apply_mask(t);
-        mx = pair_max(lane_max());
-      }
+      if (!inner) apply_mask(t);
+      const float mx = pair_max(lane_max());
       make_p();
       presum();
-      const bool need = fast ? psum_big()
-                             : (mx > kRescale) || (m_run == kNegInf && mx != kNegInf);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        if (fast) mx = pair_max(lane_max());
+      if (__builtin_amdgcn_ballot_w64((mx > kRescale) || (m_run == kNegInf && mx != kNegInf))) {
         rescale(mx);
         presum();
       }
@@ -1383,7 +1377,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) l_vec = TI::rowsum(psum[e], l_vec);
       }
-      if (!fast) started = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
+      started = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
     } else {
 #pragma unroll
       for (int g16 = 0; g16 < NG; ++g16) {
@@ -1392,6 +1386,22 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       }
       psum = u32x4{0, 0, 0, 0};
     }
+  };
+  // The fp16 fast V phase, run by fast iterations only (the tile t = t_lo +
+  // 2 (j + 1) + grp is visited and interior, and every row holds a
+  // reference max).  An earlier tile of the wave went through the general V
+  // phase and set v_first, so only the count and the last tile move here.
+  auto v_fast = [&](int j) __attribute__((always_inline)) {
+    ++v_count;
+    v_last = t_lo + 2 * (j + 1) + grp;
+    make_p();
+    presum();
+    if (__builtin_amdgcn_ballot_w64(psum_big())) {
+      rescale(pair_max(lane_max()));
+      presum();
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l_vec = TI::rowsum(psum[e], l_vec);
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1459,22 +1469,62 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   read_k(0);
   if (grp == 1) barrier();  // group 1 runs one phase behind group 0
 
-  for (int j = -1; j < n_stages; ++j) {
+  // Fast iterations: steady (0 <= j < n_stages - NS, so tile j + NS is
+  // always issued and NS - 3 tiles stay in flight at the wait) and, for fp16,
+  // the V phase's tile t = t_lo + 2 (j + 1) + grp in the wave's interior run,
+  // after at least one interior tile went through the general V phase.
+  // There the V phase forms P against the current reference at once (no row
+  // max) and raises the reference only if some pre-added P exceeds 2^10
+  // (each p <= 2^10 otherwise, so the fp16 P and its pre-added sums stay
+  // finite).  They are iterations jf_lo .. jf_end - 1, with
+  // 0 <= jf_lo <= jf_end <= n_stages - NS, or none (jf_lo = jf_end =
+  // n_stages).
+  int jf_lo = n_stages, jf_end = n_stages;
+  if (TI::kPrescaleQ && wave_live && tf_hi >= tf_lo) {
+    const int j_first = (tf_lo - t_lo - grp + 1) / 2 - 1;  // first j with t >= tf_lo
+    const int j_last = (tf_hi - t_lo - grp) / 2 - 1;       // last j with t <= tf_hi
+    const int lo = max(j_first + 1, 0), hi = min(j_last, n_stages - NS - 1);
+    if (hi >= lo) {
+      jf_lo = lo;
+      jf_end = hi + 1;
+    }
+  }
+  // One iteration: M_j then V_j.
+  auto iteration = [&](int j, auto fast) __attribute__((always_inline)) {
+    constexpr bool kFast = decltype(fast)::value;
     // ---- M_j ----
     __builtin_amdgcn_s_setprio(1);
     m_phase(j);
     // the direct loads go after the MFMAs: issued while the last ones drain
     __builtin_amdgcn_sched_barrier(0);
-    if (j >= 0 && j + NS < n_stages) load_tile(j + NS);
+    if (kFast || (j >= 0 && j + NS < n_stages)) load_tile(j + NS);
     if (paged && j >= 0 && j + NS + 1 < n_stages) fetch_rows(j + NS + 1);
     __builtin_amdgcn_s_setprio(0);
     barrier();
     // ---- V_j ----
-    v_phase(j);
-    wait_tiles(j);
+    if constexpr (kFast) {
+      v_fast(j);
+      if constexpr (NS >= 5)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
+      else if constexpr (NS == 4)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+      v_phase(j);
+      wait_tiles(j);
+    }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads done
     barrier();
-  }
+  };
+  // three runs of iterations, one loop each (one V-phase variant per loop
+  // body keeps the register allocation of the single-loop form); `started`
+  // fails only for non-finite scores, and then every iteration is general
+  int j = -1;
+  for (; j < jf_lo; ++j) iteration(j, std::false_type{});
+  if (started)
+    for (; j < jf_end; ++j) iteration(j, std::true_type{});
+  for (; j < n_stages; ++j) iteration(j, std::false_type{});
   // the last prefetch reads must be done before LDS is reused for the merge
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   if (grp == 0) barrier();
