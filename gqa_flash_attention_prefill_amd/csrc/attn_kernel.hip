@@ -997,7 +997,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   constexpr int DB = D / 32;
   constexpr int LPW = SLOT_CH / 64 / R;     // 1-KB direct loads per wave per tile
   constexpr float kRescale = 8.f;
-  constexpr uint16_t kPsumMax = 0x6400;  // fp16 1024
+  constexpr float kTileSumMax = 1024.f;  // fast-path bound on a tile's P sum per lane
   static_assert(NS == 4 || NS == 5, "ring of 4 or 5 tiles per group");
   static_assert(NB <= 2, "one -m splat per 32-key block (negm, negm1)");
   static_assert(SLOT_CH % (64 * R) == 0, "direct loads tile a slot");
@@ -1128,6 +1128,21 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
         voff -= (uint32_t)(ld_key[i] - r) * (D * 2);
       }
       lds_dma16(tile, voff, st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
+    }
+  };
+
+  // Stage j < n_stages - 1 of this group: tile t_lo + 2 j + grp < t_hi, so
+  // no clamp to t_hi and no key past the end of the keys (dense layout).
+  auto load_inner_tile = [&](int j) __attribute__((always_inline)) {
+    const int t = t_lo + 2 * j + grp;
+    const uint32_t st = ring_addr + (uint32_t)((j % NS) * SLOT_CH) * 16u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int qi = rg * LPW + i;
+      const int tt = qi / (TILE_CH / 64);
+      const int blk = qi % (TILE_CH / 64);
+      const char* tile = reinterpret_cast<const char*>(tt ? vptr : kptr) + (int64_t)t * (BKV * D * 2);
+      lds_dma16(tile, ld_off[i], st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
     }
   };
 
@@ -1335,19 +1350,6 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       for (int i = 0; i < 16; ++i) sc[nb][i] += shift;
     make_p();
   };
-  // Does some element of the pre-added P exceed 2^10 (or is it inf / NaN)?
-  // Non-negative fp16 values order as their bit patterns.  The four words
-  // are copied out first: hipcc lowers a __builtin_bit_cast of a vector
-  // element (psum[i] directly) to a load of element 0 whatever i is.
-  auto psum_big = [&]() __attribute__((always_inline)) {
-    const uint32_t w0 = psum[0], w1 = psum[1], w2 = psum[2], w3 = psum[3];
-    u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w0),
-                                        __builtin_bit_cast(u16x2, w1));
-    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w2),
-                                              __builtin_bit_cast(u16x2, w3));
-    a = __builtin_elementwise_max(a, b);
-    return a[0] > kPsumMax || a[1] > kPsumMax;
-  };
 
   // One V phase: softmax of S_{j+1} into P_{j+1} (the general path: boundary
   // tiles, a wave's first tiles, bf16, and iterations outside the steady
@@ -1389,19 +1391,29 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   };
   // The fp16 fast V phase, run by fast iterations only (the tile t = t_lo +
   // 2 (j + 1) + grp is visited and interior, and every row holds a
-  // reference max).  An earlier tile of the wave went through the general V
-  // phase and set v_first, so only the count and the last tile move here.
+  // reference max).  P is formed against the current reference; the lane's
+  // sum of it over the tile (the pre-added fp16 words, summed in fp32 by
+  // v_dot2c) bounds every P and every pre-added word, so when it is at most
+  // 2^10 nothing overflowed fp16 and P stands; otherwise (or inf / NaN) the
+  // reference is raised and P formed again.  An earlier tile of the wave
+  // went through the general V phase and set v_first, so only the count and
+  // the last tile move here.
   auto v_fast = [&](int j) __attribute__((always_inline)) {
     ++v_count;
     v_last = t_lo + 2 * (j + 1) + grp;
     make_p();
     presum();
-    if (__builtin_amdgcn_ballot_w64(psum_big())) {
+    float tsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tsum = TI::rowsum(psum[e], tsum);
+    if (__builtin_amdgcn_ballot_w64(!(tsum <= kTileSumMax))) {
       rescale(pair_max(lane_max()));
       presum();
-    }
+      tsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) l_vec = TI::rowsum(psum[e], l_vec);
+      for (int e = 0; e < 4; ++e) tsum = TI::rowsum(psum[e], tsum);
+    }
+    l_vec += tsum;
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1469,21 +1481,22 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   read_k(0);
   if (grp == 1) barrier();  // group 1 runs one phase behind group 0
 
-  // Fast iterations: steady (0 <= j < n_stages - NS, so tile j + NS is
-  // always issued and NS - 3 tiles stay in flight at the wait) and, for fp16,
+  // Fast iterations: steady (0 <= j < n_stages - NS - 1, so tile j + NS is
+  // always issued, is not the group's last tile, and NS - 3 tiles stay in
+  // flight at the wait) and, for fp16,
   // the V phase's tile t = t_lo + 2 (j + 1) + grp in the wave's interior run,
   // after at least one interior tile went through the general V phase.
   // There the V phase forms P against the current reference at once (no row
-  // max) and raises the reference only if some pre-added P exceeds 2^10
-  // (each p <= 2^10 otherwise, so the fp16 P and its pre-added sums stay
-  // finite).  They are iterations jf_lo .. jf_end - 1, with
-  // 0 <= jf_lo <= jf_end <= n_stages - NS, or none (jf_lo = jf_end =
+  // max) and raises the reference only if the lane's sum of P over the tile
+  // exceeds 2^10 (each p and each pre-added sum is at most that otherwise,
+  // so the fp16 P stays finite).  They are iterations jf_lo .. jf_end - 1, with
+  // 0 <= jf_lo <= jf_end <= n_stages - NS - 1, or none (jf_lo = jf_end =
   // n_stages).
   int jf_lo = n_stages, jf_end = n_stages;
   if (TI::kPrescaleQ && wave_live && tf_hi >= tf_lo) {
     const int j_first = (tf_lo - t_lo - grp + 1) / 2 - 1;  // first j with t >= tf_lo
     const int j_last = (tf_hi - t_lo - grp) / 2 - 1;       // last j with t <= tf_hi
-    const int lo = max(j_first + 1, 0), hi = min(j_last, n_stages - NS - 1);
+    const int lo = max(j_first + 1, 0), hi = min(j_last, n_stages - NS - 2);
     if (hi >= lo) {
       jf_lo = lo;
       jf_end = hi + 1;
@@ -1497,7 +1510,14 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     m_phase(j);
     // the direct loads go after the MFMAs: issued while the last ones drain
     __builtin_amdgcn_sched_barrier(0);
-    if (kFast || (j >= 0 && j + NS < n_stages)) load_tile(j + NS);
+    if constexpr (kFast) {
+      if (paged)
+        load_tile(j + NS);
+      else
+        load_inner_tile(j + NS);
+    } else if (j >= 0 && j + NS < n_stages) {
+      load_tile(j + NS);
+    }
     if (paged && j >= 0 && j + NS + 1 < n_stages) fetch_rows(j + NS + 1);
     __builtin_amdgcn_s_setprio(0);
     barrier();
