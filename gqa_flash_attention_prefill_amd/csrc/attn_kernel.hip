@@ -973,11 +973,15 @@ __global__ __launch_bounds__(R * (D >= 128 ? 1 : S_REQ) * 64, (D <= 128 ? 2 : 1)
 // Ping-pong variant: 8 waves = 2 groups x 4 row groups.  Group g (= KV split
 // g) takes tiles t_lo + 2 j + g.  Each wave alternates two phases separated
 // by workgroup barriers:
-//   M_j  matrix work only:  S_{j+1} = K_{j+1} . Q^T  and  O^T += V_j^T . P_j^T
-//        from fragments already in registers;
-//   V_j  vector work only:  mask / max / lazy rescale of S_{j+1}, P_{j+1} =
-//        exp2(S_{j+1}) packed to 16 bits, row sums; the direct loads of tile
-//        j + NS; the LDS reads of the K_{j+2} and V_{j+1} fragments.
+//   M_j  matrix work:  S_{j+1} = K_{j+1} . Q^T  and  O^T += V_j^T . P_j^T
+//        from fragments already in registers, each fragment register
+//        refilled (LDS reads of K_{j+2} and V_{j+1}) after the MFMA that
+//        follows its reader; then the direct loads of tile j + NS;
+//   V_j  vector work:  P_{j+1} = exp2(S_{j+1}) packed to 16 bits and its row
+//        sums (boundary and early tiles: mask, row max and lazy rescale
+//        first; interior tiles in the fast loop: P at once, the reference
+//        raised only when the tile's P sum says so); the waits for the next
+//        tiles and for this wave's fragment reads.
 // Group 1 starts one phase late, so on every SIMD (one wave of each group)
 // one wave's MFMA burst runs beside the other wave's exp2 / VALU burst.
 // Each group owns an NS-slot ring of (K, V) tiles in LDS, filled by its own
@@ -1317,7 +1321,7 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // threshold (rare: early tiles, rising scores) is the reference raised,
   // O and l rescaled and P formed again.
   // fp16: the tile's four 16-key P vectors added as packed fp16 (whole-vector
-  // adds), the operand of the tile's one row-sum MFMA in the next M phase
+  // adds); the four pre-added words give the row sum (v_dot2c)
   auto presum = [&]() __attribute__((always_inline)) {
     if constexpr (!TI::kSplitP) {
       f16x8 sum = __builtin_bit_cast(f16x8, pb[0]);
