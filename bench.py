@@ -13,11 +13,13 @@ Reported: useful TFLOP/s over the whole step (useful = 4 * d * H_q per kept
 (query, key) pair; masked work in visited tiles does not count) from the host
 clock around K back-to-back steps; the full-attention layers' TFLOP/s and
 fraction of the MI355X dense fp16/bf16 MFMA peak, and microseconds per layer
-call, from HIP events recorded around every launch on the launch stream in E
-further steps; median / min / p90 of the per-step times, of the per-layer
-times (12 layers x E samples per layer type) and of the first and last
-chunk's calls; the cold first call of each layer type (its tuning sweep
-included).  Beside it: the CPU oracle's throughput on a bounded row sample of
+call, from passes that run one step's calls of one layer type alone (in step
+order, back to back) between one HIP event pair on the launch stream; per-call
+times from HIP events recorded around every launch in E further steps (each
+pair adds about 2 us of queue work to its call); median / min / p90 of the
+per-step times, of the passes, of the per-layer times (12 layers x E samples
+per layer type) and of the first and last chunk's calls; the cold first call
+of each layer type (its tuning sweep included).  Beside it: the CPU oracle's throughput on a bounded row sample of
 the same workload, and one whole call of the oracle single-threaded.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--event-steps E]
@@ -902,8 +904,34 @@ def main():
     win_idx = [i for i, (layer, c, _) in enumerate(calls) if layer_window(layer) > 0]
     full_flops = sum(flops[(calls[i][0], calls[i][1])] for i in full_idx)
     win_flops = sum(flops[(calls[i][0], calls[i][1])] for i in win_idx)
-    full_ms = mean_call[full_idx].sum()
-    win_ms = mean_call[win_idx].sum()
+    # sums of the per-call event-pair times (each pair adds queue work to its call)
+    full_ms_pairs = mean_call[full_idx].sum()
+    win_ms_pairs = mean_call[win_idx].sum()
+
+    # Kind passes: one step's full-attention calls alone, in step order and back
+    # to back between a single event pair on the launch stream (likewise the
+    # window calls): each kernel's average launch duration without the per-call
+    # event pairs, which add about 2 us to every call.  The roofline and the
+    # per-kind rates come from these; per-chunk distributions from the pairs.
+    def kind_pass(idx):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in idx:
+            rc = L.attn_prefill(*calls[i][2])
+            if rc != 0:
+                raise RuntimeError(f"attn_prefill failed: {binding.attn_last_error()} ({rc})")
+        b.record(stream)
+        return a, b
+    KP = max(5, E)
+    passes = {"full": [], "window": []}
+    torch.cuda.synchronize()
+    for _ in range(KP):
+        passes["full"].append(kind_pass(full_idx))
+        passes["window"].append(kind_pass(win_idx))
+    torch.cuda.synchronize()
+    pass_ms = {k: [a.elapsed_time(b) for a, b in v] for k, v in passes.items()}
+    full_ms = float(np.median(pass_ms["full"]))
+    win_ms = float(np.median(pass_ms["window"]))
     full_tflops = full_flops / (full_ms * 1e-3) / 1e12
     win_bytes = sum(algorithmic_bytes(calls[i][1] * CHUNK, CHUNK, WINDOW) for i in win_idx)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
@@ -926,9 +954,11 @@ def main():
     full_layer = layer_ms(full_idx)
     distributions = {
         "step_ms": dist(step_ms),
+        "full_pass_ms": dist(pass_ms["full"]),
+        "window_pass_ms": dist(pass_ms["window"]),
         "full_layer_ms": dist(full_layer),
-        "full_layer_frac_peak": dist([full_flops / len(full_layer) * E / (x * 1e-3) / 1e12
-                                      / PEAK_TFLOPS_F16 for x in full_layer], 4),
+        "full_pass_frac_peak": dist([full_flops / (x * 1e-3) / 1e12 / PEAK_TFLOPS_F16
+                                     for x in pass_ms["full"]], 4),
         "window_layer_ms": dist(layer_ms(win_idx)),
         "full_call_us_chunk31": dist(chunk_us(full_idx, N_CHUNKS - 1), 2),
         "full_call_us_chunk0": dist(chunk_us(full_idx, 0), 2),
@@ -977,6 +1007,12 @@ def main():
             "full_attn_ms_per_layer": round(full_ms / (len(full_idx) / N_CHUNKS), 3),
             "window_us_per_call": round(1e3 * win_ms / len(win_idx), 2),
             "window_hbm_gbs": round(win_bytes / (win_ms * 1e-3) / 1e9, 1),
+            "kind_passes": KP,
+            "per_call_event_pairs": {
+                "full_us": round(1e3 * full_ms_pairs / len(full_idx), 2),
+                "window_us": round(1e3 * win_ms_pairs / len(win_idx), 2),
+                "full_frac_peak": round(full_flops / (full_ms_pairs * 1e-3) / 1e12
+                                        / PEAK_TFLOPS_F16, 4)},
             "us_per_layer_call": round(1e3 * (full_ms + win_ms) / len(calls), 2),
             "attn_ms_per_16k_prefill": round(full_ms + win_ms, 3),
             "frac_peak_whole_step": round(value / PEAK_TFLOPS_F16, 4),
@@ -999,6 +1035,10 @@ def main():
                                "source (its hash matches)") if traffic is not None else
                               "null: no counter record matches this kernel source",
             "kernel": "full-attention calls (window <= 0)",
+            "launch_us": round(1e3 * full_ms / len(full_idx), 2),
+            "duration_source": (f"median of {KP} passes of one step's {len(full_idx)} "
+                                "full-attention calls, in step order and back to back, between "
+                                "one HIP event pair on the launch stream"),
         },
         "cpu_baseline": cpu,
     }
