@@ -268,6 +268,8 @@ def copy_calibration(torch):
 
 
 def _classify(name):
+    if "attn_swin_kernel" in name:   # window calls only
+        return "attn_window"
     if "attn_fwd_kernel" in name or "attn_pp_kernel" in name:
         return "attn_window" if ", true," in name else "attn_full"
     if "copy" in name.lower() or "elementwise" in name.lower():

@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn_prefill.so")
 KERNEL = os.path.join(CSRC, "attn_kernel.hip")
 API = os.path.join(CSRC, "attn_api.cpp")
-N_CONFIGS = 6
+N_CONFIGS = 7
 
 # Packed-fp32 VALU instructions are disabled for all device code.
 HIPCC_FLAGS = [

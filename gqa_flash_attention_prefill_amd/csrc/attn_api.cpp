@@ -131,6 +131,15 @@ int64_t split_workspace_bytes(int64_t tokens, int64_t h_q, int64_t d, int64_t n_
 
 int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
+// Whether configuration `cfg_index` runs call `c` (KernelConfig::applies).
+bool applies(const Call& c, int cfg_index) {
+  const int hpack = gcd_int(c.h_q / c.h_kv, 32);
+  const int q_rows = attn::config(cfg_index).rows / hpack;
+  const bool split_or_noncausal = c.n_split > 1 || (c.flags & ATTN_FLAG_NONCAUSAL) != 0;
+  return attn::config_applies(cfg_index, c.d, c.window > 0 ? c.window : 0, q_rows,
+                              split_or_noncausal);
+}
+
 // Launch every sequence of `c` with configuration `cfg`.  When `log_base` is
 // non-null, records go there (the caller checked the capacity) and the number
 // written is returned in *n_records.
@@ -141,6 +150,8 @@ int run_config(const Call& c, int cfg_index, bool with_sink, int32_t* log_base,
   const int hpack = gcd_int(group, 32);
   const int q_rows = cfg.rows / hpack;
   attn::LaunchFn fn = cfg.fn[attn::d_index(c.d)][c.dtype == ATTN_BF16][c.out_dtype == ATTN_F32];
+  if (fn == nullptr || !applies(c, cfg_index))
+    return fail(ATTN_EINVAL, "configuration %s does not run this call", cfg.name);
 
   attn::Params p;
   memset(&p, 0, sizeof(p));
@@ -278,6 +289,7 @@ int sweep(const Call& c_in, int* best_out) {
   };
   for (int pass = 0; pass < kPasses && rc == ATTN_OK; ++pass) {
     for (int i = 0; i < n_cfg && rc == ATTN_OK; ++i) {
+      if (!applies(c, i)) continue;  // never chosen (its times stay infinite)
       float us = 0.f;
       if (pass == 0) {
         rc = run_config(c, i, false, nullptr, nullptr);  // warm-up
@@ -306,8 +318,8 @@ int sweep(const Call& c_in, int* best_out) {
     std::sort(v, v + kPasses);
     return v[kPasses / 2];
   };
-  int best = 0;
-  for (int i = 1; i < n_cfg; ++i)
+  int best = attn::default_config(c.d, c.dtype, c.window);
+  for (int i = 0; i < n_cfg; ++i)
     if (median(i) < median(best)) best = i;
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
@@ -450,6 +462,8 @@ int run(const Call& c_in) {
   int cfg = 0;
   rc = choose_config(c, &cfg);
   if (rc) return rc;
+  // a configuration forced onto a call it does not run: the default instead
+  if (!applies(c, cfg)) cfg = attn::default_config(c.d, c.dtype, c.window);
   int32_t* log_base = nullptr;
   if (c.log) {
     const int64_t need = plan_items(c, cfg);

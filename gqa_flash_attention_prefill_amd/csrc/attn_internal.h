@@ -52,6 +52,7 @@ struct Params {
   const int32_t* kv_idx;  // nullptr: dense caches [batch, h_kv, s_cap, d]
   uint32_t kv_row_bytes;  // bytes between consecutive pool rows (h_kv * d * 2)
   uint32_t n_pool;        // pool rows (indices are clamped below it)
+  int32_t swin_run;       // streaming window kernel: Q tiles per workgroup run (its launcher sets it)
   SeqTable seq;
 };
 
@@ -70,6 +71,10 @@ hipError_t launch_merge(const MergeParams& mp, int out_dtype_is_f32, int out_is_
 enum DType { kF16 = 1, kBF16 = 2, kF32 = 3 };
 
 using LaunchFn = hipError_t (*)(const Params&, int n_items, hipStream_t);
+// Whether a configuration runs a call: d, window (<= 0: none), chunk rows per
+// Q tile, and whether the call asks for KV splits, non-causal attention
+// (n_split > 1 or causal == 0).
+using AppliesFn = bool (*)(int d, int window, int q_rows, bool split_or_noncausal);
 
 struct KernelConfig {
   const char* name;
@@ -77,6 +82,7 @@ struct KernelConfig {
   int rows;       // Q-tile rows (q positions x packed heads)
   // indexed [d_index(d)][dtype == bf16][out is f32]
   LaunchFn fn[3][2][2];
+  AppliesFn applies;  // nullptr: every call
 };
 
 // 0: d 64, 1: d 128, 2: d 256
@@ -90,6 +96,9 @@ hipError_t noalloc_scratch(void** ptr);
 
 int config_count();
 const KernelConfig& config(int i);
+// config(i).applies to the call (a configuration that does not is never
+// swept, and a call forced onto it runs default_config instead)
+bool config_applies(int i, int d, int window, int q_rows, bool split_or_noncausal);
 int default_config(int d, int dtype, int window);
 
 }  // namespace attn

@@ -381,31 +381,21 @@ __device__ __attribute__((always_inline)) void finish_row(const Params& p, const
     p.lse[row] = any ? (m_run + __builtin_amdgcn_logf(l_kept)) * kLn2 : kNegInf;
 }
 
-// Visited-tile record of one workgroup (layout: attn_tile_log in
-// attn_prefill.h).  Each wave reports the first and last tile whose scores it
-// used and how many; the waves meet in LDS and thread 0 writes the record:
-// per wave its own three numbers, and for the work item the union of the
-// waves' tiles.  Wave w serves row group w % R and takes every S-th tile of
-// the range from its offset w / R, so the waves of one offset visit runs of
-// one residue class: their union is counted by merging the R runs (sorted by
-// first tile), two runs joining when the gap between them is at most S.
-// Row group r covers Q-tile rows [r ROWS_PER_WAVE, (r + 1) ROWS_PER_WAVE).
+// One visited-tile record (layout: attn_tile_log in attn_prefill.h) from
+// the (first, last, count) triples of the NW = R * S waves that served one
+// work item, wl[3 w .. 3 w + 2]: per wave its own three numbers, and for the
+// work item the union of the waves' tiles.  Wave w serves row group w % R
+// and takes every S-th tile of the range from its offset w / R, so the waves
+// of one offset visit runs of one residue class: their union is counted by
+// merging the R runs (sorted by first tile), two runs joining when the gap
+// between them is at most S.  Row group r covers Q-tile rows
+// [r ROWS_PER_WAVE, (r + 1) ROWS_PER_WAVE).
 template <int R, int S, int ROWS_PER_WAVE = 32>
-__device__ __attribute__((always_inline)) void write_tile_log(const Params& p, void* lds_raw,
-                                                              int wave, int v_first, int v_last,
-                               int v_count, int slot, int h_first, int q0, int q_last) {
+__device__ __attribute__((always_inline)) void store_tile_record(
+    int32_t* rec, const int* wl, int slot, int h_first, int hpack, int q0, int q_last,
+    int part, int n_parts) {
   constexpr int NW = R * S;
   static_assert(NW <= kLogMaxWaves, "record holds every wave");
-  int* wl = reinterpret_cast<int*>(lds_raw);
-  __syncthreads();  // every LDS read of the epilogue has finished
-  if ((threadIdx.x & 63) == 0) {
-    wl[3 * wave + 0] = v_first;
-    wl[3 * wave + 1] = v_last;
-    wl[3 * wave + 2] = v_count;
-  }
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kLogFields;
   int t_first = 0x7fffffff, t_last = -1, n_visited = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -448,7 +438,7 @@ __device__ __attribute__((always_inline)) void write_tile_log(const Params& p, v
   }
   rec[0] = slot;
   rec[1] = h_first;
-  rec[2] = p.hpack;
+  rec[2] = hpack;
   rec[3] = q0;
   rec[4] = q_last;
   rec[5] = n_visited > 0 ? t_first : -1;
@@ -456,8 +446,8 @@ __device__ __attribute__((always_inline)) void write_tile_log(const Params& p, v
   rec[7] = n_visited;
   rec[8] = NW;
   rec[9] = S;
-  rec[10] = blockIdx.y;
-  rec[11] = gridDim.y;
+  rec[10] = part;
+  rec[11] = n_parts;
 #pragma unroll
   for (int i = 13; i < 16; ++i) rec[i] = 0;
   rec[12] = ROWS_PER_WAVE;
@@ -467,6 +457,27 @@ __device__ __attribute__((always_inline)) void write_tile_log(const Params& p, v
     rec[16 + 3 * w + 1] = w < NW ? wl[3 * w + 1] : -1;
     rec[16 + 3 * w + 2] = w < NW ? wl[3 * w + 2] : 0;
   }
+}
+
+// Visited-tile record of one workgroup: each wave reports the first and last
+// tile whose scores it used and how many; the waves meet in LDS and thread 0
+// writes the record (store_tile_record).
+template <int R, int S, int ROWS_PER_WAVE = 32>
+__device__ __attribute__((always_inline)) void write_tile_log(const Params& p, void* lds_raw,
+                                                              int wave, int v_first, int v_last,
+                               int v_count, int slot, int h_first, int q0, int q_last) {
+  int* wl = reinterpret_cast<int*>(lds_raw);
+  __syncthreads();  // every LDS read of the epilogue has finished
+  if ((threadIdx.x & 63) == 0) {
+    wl[3 * wave + 0] = v_first;
+    wl[3 * wave + 1] = v_last;
+    wl[3 * wave + 2] = v_count;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int32_t* rec = p.log + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kLogFields;
+  store_tile_record<R, S, ROWS_PER_WAVE>(rec, wl, slot, h_first, p.hpack, q0, q_last,
+                                         blockIdx.y, gridDim.y);
 }
 
 // This workgroup's part of the Q tile's KV tiles [t_lo, t_hi] when the range
@@ -1613,6 +1624,393 @@ hipError_t launch_pp(const Params& p, int n_items, hipStream_t stream) {
 }
 
 
+// ---------------------------------------------------------------------------
+// Streaming window kernel, for sliding windows much shorter than the chunk.
+// One workgroup walks a run of consecutive Q tiles of one sequence, KV head
+// and head group.  Its eight waves form two streams of four 32-row waves:
+// stream s takes tile j + s of each pair (j, j + 1), and both read the
+// window's K/V from one LDS ring of 32-key blocks (block kb in slot kb % NR).
+// Consecutive tiles share all but q_rows of their keys, so each pair loads
+// only the blocks the next pair adds -- issued at the pair's start, waited
+// for at its end -- instead of a whole window per tile; and each wave loads
+// the Q of its next tile into its Q registers as soon as its last S MFMA has
+// read them.  Per block a wave runs S^T = K . Q^T, the mask where the block
+// is not interior to its rows, the online softmax with the lazy rescale, and
+// O^T += V^T . P^T, as attn_fwd_kernel does per tile; the two streams' waves
+// share each SIMD, one's matrix work beside the other's vector work.
+// Causal, window > 0, one KV part; XTRA adds the log-sum-exp output and the
+// token-pool layout.  The ring holds two pairs' keys when
+// (4 q_rows + window - 2) / 32 + 2 <= NR (swin_applies).
+constexpr int kSwinRing = 9;
+
+bool swin_applies(int d, int window, int q_rows, bool split_or_noncausal) {
+  return !split_or_noncausal && window > 0 && (d == 64 || d == 128) && q_rows > 0 &&
+         ((int64_t)4 * q_rows + window - 2) / 32 + 2 <= kSwinRing;
+}
+
+template <int D, bool XTRA, typename TI, typename TO>
+__global__ __launch_bounds__(512) void attn_swin_kernel(Params p) {
+  constexpr int BKV = 32;
+  constexpr int R = 4;                  // row waves per stream
+  constexpr int NW = 2 * R;
+  constexpr int NR = kSwinRing;
+  constexpr int DCH = D / 8;
+  constexpr int BLK_CH = BKV * DCH;     // 16-byte chunks of one K (or V) block
+  constexpr int SLOT_CH = 2 * BLK_CH;   // K, then V
+  constexpr int KSTEPS = D / 16;
+  constexpr int NG = BKV / 16;
+  constexpr int DB = D / 32;
+  constexpr int PPW = SLOT_CH / 64 / NW;  // 1-KB direct loads per wave per block
+  constexpr float kRescale = 8.f;
+  static_assert(SLOT_CH % (64 * NW) == 0, "direct loads tile a block");
+  static_assert(NR * SLOT_CH * 16 + 2 * NW * 3 * 4 + 64 * 16 <= 160 * 1024, "LDS");
+
+  __shared__ u32x4 ring[NR * SLOT_CH];
+  __shared__ int rec_wl[2][NW * 3];     // per pair parity: each wave's (first, last, count)
+  __shared__ u32x4 pf_sink[64];         // landing place of the Q prefetch (never read)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % R;
+  const int st = wave / R;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // ---- the run: KV head g, head group hg, sequence b, its tiles j_first .. j_last ----
+  const int h_kv = p.h_kv, n_hg = p.n_hgroups, run = max(1, p.swin_run);
+  const int g = blockIdx.x % h_kv;
+  const int r0 = blockIdx.x / h_kv;
+  const int hg = r0 % n_hg;
+  int rr = r0 / n_hg;  // run index over the sequences, ceil(tiles / run) runs each
+  int b = 0;
+  for (;;) {
+    const int nr_b = (p.seq.cu_tiles[b + 1] - p.seq.cu_tiles[b] + run - 1) / run;
+    if (rr < nr_b || b + 1 >= p.seq.n_seq) break;
+    rr -= nr_b;
+    ++b;
+  }
+  const int nt = p.seq.cu_tiles[b + 1] - p.seq.cu_tiles[b];
+  const int j_first = rr * run;
+  const int j_last = min(nt, j_first + run) - 1;
+  if (j_first > j_last) return;  // the whole workgroup: nothing to do
+  const int cu0 = p.seq.cu_q[b];
+  const int sq = p.seq.cu_q[b + 1] - cu0;
+  const int past = p.seq.past[b];
+  const int slot = p.seq.slot[b];
+  const int skv = past + sq;
+  const int W = p.window;
+  const int q_rows = p.q_rows;
+  const int tile0 = p.seq.cu_tiles[b];
+  const float c = p.scale_log2;
+  const float kNegInf = -__builtin_inff();
+
+  const int row = rg * 32 + col;
+  const int psub = row / p.hpack;  // position within the Q tile
+  const int head = g * p.group + hg * p.hpack + row % p.hpack;
+  const float sink = load_sink(p.sink, head);
+
+  // Token-pool layout (XTRA only): key k of this sequence is pool row
+  // kv_list[k], rows h_kv * d elements apart; otherwise the dense cache of
+  // this sequence's slot and KV head.
+  const bool paged = XTRA && p.kv_idx != nullptr;
+  const int32_t* kv_list = paged ? p.kv_idx + p.seq.kv_start[b] : nullptr;
+  const int64_t kv_base =
+      paged ? (int64_t)g * D : ((int64_t)slot * h_kv + g) * (int64_t)p.s_cap * D;
+  const uint16_t* kptr = reinterpret_cast<const uint16_t*>(p.k) + kv_base;
+  const uint16_t* vptr = reinterpret_cast<const uint16_t*>(p.v) + kv_base;
+  const uint32_t ring_addr = lds_byte_addr(ring);
+
+  // ---- direct loads: wave w issues pieces w * PPW + i of a block's 2 * BLK_CH
+  // / 64 one-KB pieces (K, then V); lane l of a piece fills chunk 64 * piece + l
+  // of its tensor block: key (64 * piece + l) / DCH, physical chunk l % DCH ----
+  int ld_key[PPW];
+  uint32_t ld_off[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int qi = wave * PPW + i;
+    const int tt = qi / (BLK_CH / 64);
+    const int chunk = (qi % (BLK_CH / 64)) * 64 + lane;
+    const int key = chunk / DCH;
+    const int pch = chunk % DCH;
+    const int ch = tt ? v_chunk<D>(key, pch) : k_chunk<D>(key, pch);
+    ld_key[i] = key;
+    ld_off[i] = (uint32_t)(key * D + ch * 8) * 2u;
+  }
+  // Blocks kb_from .. kb_to (at most NR) into their slots; rows at or past
+  // skv read row skv - 1 (finite data whose scores the causal mask removes).
+  auto load_blocks = [&](int kb_from, int kb_to) __attribute__((always_inline)) {
+    uint32_t prow[NR][PPW];
+    if (paged) {
+      // every pool row first, then the loads (one index round trip)
+#pragma unroll
+      for (int n = 0; n < NR; ++n)
+#pragma unroll
+        for (int i = 0; i < PPW; ++i)
+          prow[n][i] = kb_from + n <= kb_to
+                           ? (uint32_t)kv_list[min((kb_from + n) * BKV + ld_key[i], skv - 1)]
+                           : 0u;
+    }
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      const int kb = kb_from + n;
+      if (kb > kb_to) break;
+      const uint32_t dst = ring_addr + (uint32_t)((kb % NR) * SLOT_CH) * 16u;
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        const int qi = wave * PPW + i;
+        const int tt = qi / (BLK_CH / 64);
+        const int blk = qi % (BLK_CH / 64);
+        const uint32_t ldst = dst + (uint32_t)(tt * BLK_CH + blk * 64) * 16u;
+        if (paged) {
+          const uint32_t r = min(prow[n][i], p.n_pool - 1u);
+          lds_dma16(tt ? vptr : kptr, r * p.kv_row_bytes + ld_off[i] - (uint32_t)ld_key[i] * (D * 2),
+                    ldst);
+          continue;
+        }
+        const char* blkp =
+            reinterpret_cast<const char*>(tt ? vptr : kptr) + (int64_t)kb * (BKV * D * 2);
+        uint32_t voff = ld_off[i];
+        if (kb * BKV + BKV > skv) {
+          const int r = min(ld_key[i], skv - 1 - kb * BKV);
+          voff -= (uint32_t)(ld_key[i] - r) * (D * 2);
+        }
+        lds_dma16(blkp, voff, ldst);
+      }
+    }
+  };
+  // blocks of the pair starting at tile j: from the first row's window floor
+  // to the key of the pair's last row
+  auto pair_lo = [&](int j) __attribute__((always_inline)) {
+    return max(0, past + j * q_rows - W + 1) / BKV;
+  };
+  auto pair_hi = [&](int j) __attribute__((always_inline)) {
+    const int je = min(j + 1, j_last);
+    return (past + min((je + 1) * q_rows, sq) - 1) / BKV;
+  };
+
+  // Q^T fragments of this lane's row of tile jt (rows past the chunk read its
+  // last row; prepare_q zeroes them)
+  u32x4 qf[KSTEPS];
+  auto load_q = [&](int jt) __attribute__((always_inline)) {
+    const int pos = jt * q_rows + psub;
+    const int64_t qoff = ((int64_t)(cu0 + min(pos, sq - 1)) * p.h_q + head) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = load16<TI>(p.q, qoff + kk * 16);
+  };
+
+  // The Q rows of this stream's tile jt brought into L2 a pair ahead: one
+  // 16-byte direct load into pf_sink per 128-byte line of the tile's 2 D
+  // lines (each position's hpack rows are hpack D / 64 consecutive lines),
+  // one load a wave, so that the register loads at the end of the previous
+  // tile find them in L2 instead of HBM.
+  const uint32_t pf_addr = lds_byte_addr(pf_sink);
+  auto prefetch_q = [&](int jt) __attribute__((always_inline)) {
+    const int q0 = jt * q_rows;
+    const char* qtile = reinterpret_cast<const char*>(p.q) +
+                        (((int64_t)(cu0 + q0) * p.h_q + g * p.group + hg * p.hpack) * D) * 2;
+    const int lpp = p.hpack * D / 64;             // lines per position
+    const int line = (rg * 64 + lane) % (2 * D);  // the tile's lines
+    const int pr = min(q0 + line / lpp, sq - 1) - q0;  // positions past the chunk: its last
+    lds_dma16(qtile, (uint32_t)((pr * p.h_q * D + (line % lpp) * 64) * 2), pf_addr);
+  };
+
+  // One Q tile of this wave's stream: every block of its rows' window, then
+  // the epilogue; the visited blocks are noted in (*vf, *vl, *vc).
+  auto tile = [&](int jt, int* vf, int* vl, int* vc) __attribute__((always_inline)) {
+    const int q0 = jt * q_rows;
+    const int pos = q0 + psub;
+    const bool valid = pos < sq;
+    const int row_hi = past + pos;           // last kept key
+    const int row_lo = past + pos - W + 1;   // first kept key
+    const int wp0 = q0 + (rg * 32) / p.hpack;
+    const int wp1 = min(q0 + (rg * 32 + 31) / p.hpack, sq - 1);
+    const bool wave_live = wp0 < sq;
+    const int w_lo = max(0, past + wp0 - W + 1) / BKV;
+    const int w_hi = (past + wp1) / BKV;
+    const int w_full_lo = past + wp1 - W + 1;  // max row lower bound
+    const int w_full_hi = past + wp0;          // min row upper bound
+    const bool next = jt + 2 <= j_last;
+    prepare_q<TI, KSTEPS>(qf, c, valid);
+    float m_run = kNegInf, l_run = 0.f, m_use = 0.f;
+    f32x16 negm = f32x16{};  // splat(-m_use): MFMA accumulator input (prescaled-Q path)
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    if (wave_live) {
+      for (int kb = w_lo; kb <= w_hi; ++kb) {
+        const u32x4* kt = ring + (kb % NR) * SLOT_CH;
+        const u32x4* vt = kt + BLK_CH;
+        // S^T in two accumulation chains (even and odd k-steps), so that
+        // consecutive MFMAs do not wait for each other's results (one chain
+        // for fp16 at d 128, whose -m splat leaves no registers for a second)
+        f32x16 sc = TI::mma(kt[col * DCH + k_chunk<D>(col, half)], qf[0],
+                            TI::kPrescaleQ ? negm : f32x16{});
+        if constexpr (TI::kPrescaleQ && D >= 128) {
+#pragma unroll
+          for (int kk = 1; kk < KSTEPS; ++kk)
+            sc = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + half)], qf[kk], sc);
+        } else {
+          f32x16 sc2 = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 + half)], qf[1], f32x16{});
+#pragma unroll
+          for (int kk = 2; kk < KSTEPS; kk += 2) {
+            sc = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + half)], qf[kk], sc);
+            sc2 = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + 2 + half)], qf[kk + 1], sc2);
+          }
+          sc += sc2;
+        }
+        // the last S of this tile has read qf: the next tile's Q goes in
+        if (kb == w_hi && next) load_q(jt + 2);
+        if constexpr (!TI::kPrescaleQ) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c, -m_use);
+        }
+        const int kbase = kb * BKV;
+        if (!((kbase + BKV - 1 <= w_full_hi) && (kbase >= w_full_lo))) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + (i >> 2) * 8 + half * 4 + (i & 3);
+            if (key > row_hi || key < row_lo) sc[i] = kNegInf;
+          }
+        }
+        float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+        for (int i = 0; i < 16; i += 2)
+          m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[i], sc[i + 1]));
+        const float mx = pair_max(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])));
+        // raise the reference max where the block needs it (wave-uniform)
+        if (__builtin_amdgcn_ballot_w64((mx > kRescale) || (m_run == kNegInf && mx != kNegInf))) {
+          const float m_new = fmaxf(m_run, mx + m_use);
+          const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+          m_run = m_new;
+          const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
+          const float shift = m_use - m_use_new;
+          m_use = m_use_new;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[i] += shift;
+        }
+        if (*vc == 0) *vf = kb;
+        *vl = kb;
+        ++*vc;
+        // P = exp2(S), 16-bit (bf16: hi + lo parts), and its row sum
+        u32x4 pb[NG], pl[NG];
+        float rs = 0.f;
+#pragma unroll
+        for (int g16 = 0; g16 < NG; ++g16)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int i = (g16 & 1) * 8 + w * 2;
+            const float p0 = __builtin_amdgcn_exp2f(sc[i]);
+            const float p1 = __builtin_amdgcn_exp2f(sc[i + 1]);
+            const uint32_t hi = TI::pack(p0, p1);
+            pb[g16][w] = hi;
+            if constexpr (TI::kSplitP) {
+              pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
+              rs += p0 + p1;
+            } else {
+              rs = TI::rowsum(hi, rs);
+            }
+          }
+        l_run += rs;
+        // P.V, consecutive MFMAs on different output blocks (bf16: every
+        // block's hi part, then its lo part)
+#pragma unroll
+        for (int g16 = 0; g16 < NG; ++g16) {
+          u32x4 a[DB];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) a[db] = v_frag<D>(vt, g16, db, lane);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = TI::mma(a[db], pb[g16], acc[db]);
+          if constexpr (TI::kSplitP) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] = TI::mma(a[db], pl[g16], acc[db]);
+          }
+        }
+      }
+    } else if (next) {
+      load_q(jt + 2);
+    }
+    const float l_kept = l_run + other_half(l_run);
+    if (valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_kept, sink, cu0 + pos, head, half);
+  };
+
+  // ---- prologue: the first pair's blocks and each stream's first Q ----
+  int ring_hi = pair_hi(j_first);
+  load_blocks(pair_lo(j_first), ring_hi);
+  if (j_first + st <= j_last) load_q(j_first + st);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  int par = 0;
+  for (int j = j_first; j <= j_last; j += 2, par ^= 1) {
+    // the blocks the next pair adds: their slots held blocks below this
+    // pair's floor (the ring holds both pairs' keys)
+    if (j + 2 <= j_last) {
+      const int nh = pair_hi(j + 2);
+      if (nh > ring_hi) {
+        load_blocks(ring_hi + 1, nh);
+        ring_hi = nh;
+      }
+    }
+    const int jt = j + st;
+    if (jt + 2 <= j_last) prefetch_q(jt + 2);
+    int v_first = -1, v_last = -1, v_count = 0;
+    if (jt <= j_last) tile(jt, &v_first, &v_last, &v_count);
+    if (p.log != nullptr && lane == 0) {
+      rec_wl[par][3 * wave + 0] = v_first;
+      rec_wl[par][3 * wave + 1] = v_last;
+      rec_wl[par][3 * wave + 2] = v_count;
+    }
+    // next pair's blocks and Q landed; every wave done with this pair's blocks
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (p.log != nullptr && lane == 0 && rg == 0 && jt <= j_last) {
+      const int64_t item = ((int64_t)(tile0 + jt) * n_hg + hg) * h_kv + g;
+      store_tile_record<R, 1>(p.log + item * kLogFields, &rec_wl[par][3 * R * st], slot,
+                              g * p.group + hg * p.hpack, p.hpack, jt * q_rows,
+                              min((jt + 1) * q_rows, sq) - 1, 0, 1);
+    }
+  }
+}
+
+template <int D, bool XTRA, typename TI, typename TO>
+void launch_swin_x(const Params& p, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_swin_kernel<D, XTRA, TI, TO>), dim3(grid), dim3(512), 0, stream, p);
+}
+
+// Runs of an even number of Q tiles (both streams busy), a run within one
+// sequence: the shortest runs whose workgroups all fit the chip at once (one
+// per CU: eight waves of 160-250 VGPRs fill the register file), so that no
+// second round of a few workgroups follows the first.
+template <int D, typename TI, typename TO>
+hipError_t launch_swin(const Params& p_in, int /*n_items*/, hipStream_t stream) {
+  Params p = p_in;
+  constexpr int64_t kSlots = 256;
+  const int heads = p.h_kv * p.n_hgroups;
+  auto count_runs = [&](int run) {
+    int64_t runs = 0;
+    for (int b = 0; b < p.seq.n_seq; ++b)
+      runs += (p.seq.cu_tiles[b + 1] - p.seq.cu_tiles[b] + run - 1) / run;
+    return runs * heads;
+  };
+  int run = (int)(((int64_t)p.seq.n_tiles * heads + kSlots - 1) / kSlots);
+  run = max(2, run + (run & 1));
+  while (run < 512 && count_runs(run) > kSlots) run += 2;
+  p.swin_run = run;
+  const int64_t grid = count_runs(run);
+  if (grid <= 0) return hipSuccess;
+  if (p.lse != nullptr || p.kv_idx != nullptr)
+    launch_swin_x<D, true, TI, TO>(p, (unsigned)grid, stream);
+  else
+    launch_swin_x<D, false, TI, TO>(p, (unsigned)grid, stream);
+  return hipGetLastError();
+}
+
 template <int D, int BKV, int R, int S, int NS, bool XTRA, typename TI, typename TO>
 void launch_x(const Params& p, int n_items, hipStream_t stream) {
   constexpr int threads = R * (D >= 128 ? 1 : S) * 64;
@@ -1717,6 +2115,19 @@ constexpr KernelConfig make_pp_config(const char* name) {
         {launch<256, 32, 4, 1, 3, BF16, uint16_t>, launch<256, 32, 4, 1, 3, BF16, float>}}}};
 }
 
+// The streaming window kernel (d 64 and 128; calls it does not run fall back
+// to the default configuration, see swin_applies).
+constexpr KernelConfig make_swin_config(const char* name) {
+  return KernelConfig{
+      name, {32, 32, 32}, 128,
+      {{{launch_swin<64, F16, uint16_t>, launch_swin<64, F16, float>},
+        {launch_swin<64, BF16, uint16_t>, launch_swin<64, BF16, float>}},
+       {{launch_swin<128, F16, uint16_t>, launch_swin<128, F16, float>},
+        {launch_swin<128, BF16, uint16_t>, launch_swin<128, BF16, float>}},
+       {{nullptr, nullptr}, {nullptr, nullptr}}},
+      swin_applies};
+}
+
 }  // namespace
 
 #if defined(ATTN_CONFIG) && ATTN_CONFIG >= 0
@@ -1745,6 +2156,10 @@ ATTN_CONFIG_ENTRY(4, make_config<32, 2, 2>("r64_kv32_s2"))
 // with few rows per sequence, e.g. decode steps (one position x the KV
 // group's heads)
 ATTN_CONFIG_ENTRY(5, make_config<32, 1, 2>("r32_kv32_s2"))
+#elif ATTN_CONFIG == 6
+// streaming window kernel: runs of consecutive 128-row Q tiles per workgroup
+// over an LDS ring of 32-key blocks (window calls of long chunks)
+ATTN_CONFIG_ENTRY(6, make_swin_config("swin_r128_kv32"))
 #else
 #error "ATTN_CONFIG out of range"
 #endif
@@ -1757,9 +2172,11 @@ const KernelConfig& config_entry_2();
 const KernelConfig& config_entry_3();
 const KernelConfig& config_entry_4();
 const KernelConfig& config_entry_5();
+const KernelConfig& config_entry_6();
 namespace {
 const KernelConfig& (*const kConfigs[])() = {config_entry_0, config_entry_1, config_entry_2,
-                                             config_entry_3, config_entry_4, config_entry_5};
+                                             config_entry_3, config_entry_4, config_entry_5,
+                                             config_entry_6};
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& mp, int out_is_f32, int out_is_bf16,
@@ -1810,6 +2227,10 @@ hipError_t noalloc_scratch(void** ptr) {
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
 const KernelConfig& config(int i) { return kConfigs[i](); }
 int default_config(int /*d*/, int /*dtype*/, int /*window*/) { return 0; }
+bool config_applies(int i, int d, int window, int q_rows, bool split_or_noncausal) {
+  const AppliesFn f = config(i).applies;
+  return f == nullptr || f(d, window, q_rows, split_or_noncausal);
+}
 #endif
 
 }  // namespace attn

@@ -288,6 +288,14 @@ const char* attn_last_error(void);
  * caller's cache (see "The tuning sweep" above), so that the choice made on a
  * shallow first chunk holds for the deep ones.  Environment: ATTN_PREFILL_TUNE=0 skips sweeps and uses the
  * default configuration; ATTN_PREFILL_CONFIG=<name> forces one.
+ * Some configurations run only some calls: the streaming window one
+ * ("swin_r128_kv32") needs a causal call with window > 0, one KV part, d 64
+ * or 128, and a window short enough for its ring of 32-key blocks to hold
+ * the keys of four consecutive Q tiles plus one window
+ * ((4 q_rows + window - 2) / 32 + 2 <= 9, q_rows = 128 / gcd(group, 32)).
+ * A sweep skips a configuration that does not run its call, and a call
+ * forced onto one runs the default configuration instead (its tile log
+ * reports that configuration's bkv and q_rows).
  */
 int attn_tune_stats(int64_t* sweeps, int64_t* tuning_launches, int64_t* cached_keys);
 void attn_tune_reset(void);

@@ -293,3 +293,26 @@ def test_first_call_sweep_with_poisoned_cache_tail():
     assert torch.isfinite(out).all()
     check_rows(f64(out), ref, case.name)
     check_tile_log(recs, bkv, q_rows, case.cu_seqlens, case.past, case.window, case.h_q)
+
+
+def _forced(name):
+    """Force the configuration called `name` for the calls made meanwhile."""
+    idx = [binding.attn_config_name(i) for i in range(binding.attn_config_count())].index(name)
+    binding.attn_force_config(idx)
+
+
+def test_streaming_window_full_size():
+    # The streaming window configuration at the benchmark's window shapes: the
+    # ragged bf16 d 128 batch (sampled rows, long runs of Q tiles per
+    # workgroup over the block ring) and the 512-row window chunks at past 0
+    # and 8192 (whole outputs); it runs these calls itself (bkv 32).
+    try:
+        _forced("swin_r128_kv32")
+        _sampled_check(synth.ragged_bf16(), n_rows=4096, seed=3)
+        for past in (0, 8192):
+            _whole_check(synth.swa_chunk(past), tag=f"_swin_past{past}")
+        inp = synth.make(synth.ragged_bf16())
+        _, _, bkv, _ = _call(inp, synth.ragged_bf16(), torch.float32)
+        assert bkv == 32
+    finally:
+        binding.attn_force_config(-1)
