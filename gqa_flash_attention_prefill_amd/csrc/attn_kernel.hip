@@ -1837,104 +1837,117 @@ __global__ __launch_bounds__(512) void attn_swin_kernel(Params p) {
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-    if (wave_live) {
-      for (int kb = w_lo; kb <= w_hi; ++kb) {
-        const u32x4* kt = ring + (kb % NR) * SLOT_CH;
-        const u32x4* vt = kt + BLK_CH;
-        // S^T in two accumulation chains (even and odd k-steps), so that
-        // consecutive MFMAs do not wait for each other's results (one chain
-        // for fp16 at d 128, whose -m splat leaves no registers for a second)
-        f32x16 sc = TI::mma(kt[col * DCH + k_chunk<D>(col, half)], qf[0],
-                            TI::kPrescaleQ ? negm : f32x16{});
-        if constexpr (TI::kPrescaleQ && D >= 128) {
+    // S^T of block kb relative to the current reference (fp16: -m enters
+    // as the accumulator input; bf16: scaled and shifted on the VALU later)
+    auto scores = [&](int kb) __attribute__((always_inline)) {
+      const u32x4* kt = ring + (kb % NR) * SLOT_CH;
+      f32x16 sc = TI::mma(kt[col * DCH + k_chunk<D>(col, half)], qf[0],
+                          TI::kPrescaleQ ? negm : f32x16{});
 #pragma unroll
-          for (int kk = 1; kk < KSTEPS; ++kk)
-            sc = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + half)], qf[kk], sc);
-        } else {
-          f32x16 sc2 = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 + half)], qf[1], f32x16{});
+      for (int kk = 1; kk < KSTEPS; ++kk)
+        sc = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + half)], qf[kk], sc);
+      return sc;
+    };
+    // exp2 units (bf16), the mask where block kb is not interior to this
+    // wave's rows, the row max, and a raise of the reference max where the
+    // block needs it (wave-uniform; rescales O and l, shifts sc)
+    auto prepare = [&](int kb, f32x16& sc) __attribute__((always_inline)) {
+      if constexpr (!TI::kPrescaleQ) {
 #pragma unroll
-          for (int kk = 2; kk < KSTEPS; kk += 2) {
-            sc = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + half)], qf[kk], sc);
-            sc2 = TI::mma(kt[col * DCH + k_chunk<D>(col, 2 * kk + 2 + half)], qf[kk + 1], sc2);
-          }
-          sc += sc2;
-        }
-        // the last S of this tile has read qf: the next tile's Q goes in
-        if (kb == w_hi && next) load_q(jt + 2);
-        if constexpr (!TI::kPrescaleQ) {
+        for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c, -m_use);
+      }
+      const int kbase = kb * BKV;
+      if (!((kbase + BKV - 1 <= w_full_hi) && (kbase >= w_full_lo))) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c, -m_use);
-        }
-        const int kbase = kb * BKV;
-        if (!((kbase + BKV - 1 <= w_full_hi) && (kbase >= w_full_lo))) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (key > row_hi || key < row_lo) sc[i] = kNegInf;
-          }
-        }
-        float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-        for (int i = 0; i < 16; i += 2)
-          m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[i], sc[i + 1]));
-        const float mx = pair_max(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])));
-        // raise the reference max where the block needs it (wave-uniform)
-        if (__builtin_amdgcn_ballot_w64((mx > kRescale) || (m_run == kNegInf && mx != kNegInf))) {
-          const float m_new = fmaxf(m_run, mx + m_use);
-          const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-          m_run = m_new;
-          const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
-          const float shift = m_use - m_use_new;
-          m_use = m_use_new;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) negm[i] = -m_use;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] += shift;
-        }
-        if (*vc == 0) *vf = kb;
-        *vl = kb;
-        ++*vc;
-        // P = exp2(S), 16-bit (bf16: hi + lo parts), and its row sum
-        u32x4 pb[NG], pl[NG];
-        float rs = 0.f;
-#pragma unroll
-        for (int g16 = 0; g16 < NG; ++g16)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int i = (g16 & 1) * 8 + w * 2;
-            const float p0 = __builtin_amdgcn_exp2f(sc[i]);
-            const float p1 = __builtin_amdgcn_exp2f(sc[i + 1]);
-            const uint32_t hi = TI::pack(p0, p1);
-            pb[g16][w] = hi;
-            if constexpr (TI::kSplitP) {
-              pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
-              rs += p0 + p1;
-            } else {
-              rs = TI::rowsum(hi, rs);
-            }
-          }
-        l_run += rs;
-        // P.V, consecutive MFMAs on different output blocks (bf16: every
-        // block's hi part, then its lo part)
-#pragma unroll
-        for (int g16 = 0; g16 < NG; ++g16) {
-          u32x4 a[DB];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) a[db] = v_frag<D>(vt, g16, db, lane);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = TI::mma(a[db], pb[g16], acc[db]);
-          if constexpr (TI::kSplitP) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] = TI::mma(a[db], pl[g16], acc[db]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + (i >> 2) * 8 + half * 4 + (i & 3);
+          if (key > row_hi || key < row_lo) sc[i] = kNegInf;
         }
       }
+      float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        m4[(i >> 1) & 3] = vmax(m4[(i >> 1) & 3], vmax(sc[i], sc[i + 1]));
+      const float mx = pair_max(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3])));
+      if (__builtin_amdgcn_ballot_w64((mx > kRescale) || (m_run == kNegInf && mx != kNegInf))) {
+        const float m_new = fmaxf(m_run, mx + m_use);
+        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+        const float m_use_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float shift = m_use - m_use_new;
+        m_use = m_use_new;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] += shift;
+      }
+      if (*vc == 0) *vf = kb;
+      *vl = kb;
+      ++*vc;
+    };
+    // P = exp2(S) of block kb, 16-bit (bf16: hi + lo parts), its row sum into
+    // l_run, and O^T += V^T . P^T (consecutive MFMAs on different output
+    // blocks; bf16: every block's hi part, then its lo part)
+    auto pv = [&](int kb, const f32x16& sc) __attribute__((always_inline)) {
+      const u32x4* vt = ring + (kb % NR) * SLOT_CH + BLK_CH;
+      u32x4 pb[NG], pl[NG];
+      float rs = 0.f;
+#pragma unroll
+      for (int g16 = 0; g16 < NG; ++g16)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int i = (g16 & 1) * 8 + w * 2;
+          const float p0 = __builtin_amdgcn_exp2f(sc[i]);
+          const float p1 = __builtin_amdgcn_exp2f(sc[i + 1]);
+          const uint32_t hi = TI::pack(p0, p1);
+          pb[g16][w] = hi;
+          if constexpr (TI::kSplitP) {
+            pl[g16][w] = TI::pack(TI::lo_part(p0, hi, 0), TI::lo_part(p1, hi, 1));
+            rs += p0 + p1;
+          } else {
+            rs = TI::rowsum(hi, rs);
+          }
+        }
+      l_run += rs;
+#pragma unroll
+      for (int g16 = 0; g16 < NG; ++g16) {
+        u32x4 a[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) a[db] = v_frag<D>(vt, g16, db, lane);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = TI::mma(a[db], pb[g16], acc[db]);
+        if constexpr (TI::kSplitP) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = TI::mma(a[db], pl[g16], acc[db]);
+        }
+      }
+    };
+    if (wave_live) {
+      // two-stage pipeline: the next block's S MFMAs go out beside this
+      // block's exponentials, then this block's P.V, then the next block's
+      // mask, max and rescale (which rescales O after this block's P.V)
+      f32x16 s_cur = scores(w_lo);
+      // the last S of this tile has read qf: the next tile's Q goes in
+      if (w_lo == w_hi && next) load_q(jt + 2);
+      prepare(w_lo, s_cur);
+      for (int kb = w_lo; kb < w_hi; ++kb) {
+        f32x16 s_nxt = scores(kb + 1);
+        pv(kb, s_cur);
+        if (kb + 1 == w_hi && next) load_q(jt + 2);
+        prepare(kb + 1, s_nxt);
+        s_cur = s_nxt;
+      }
+      pv(w_hi, s_cur);
     } else if (next) {
       load_q(jt + 2);
     }
+    // this pair's block loads and the next tile's Q landed; waited for here,
+    // before the stores, since the vector-memory counter also counts stores
+    // (the stores then complete under the next pair)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const float l_kept = l_run + other_half(l_run);
     if (valid) finish_row<D, XTRA, TI, TO>(p, acc, m_run, l_kept, sink, cu0 + pos, head, half);
   };
@@ -1966,8 +1979,9 @@ __global__ __launch_bounds__(512) void attn_swin_kernel(Params p) {
       rec_wl[par][3 * wave + 1] = v_last;
       rec_wl[par][3 * wave + 2] = v_count;
     }
-    // next pair's blocks and Q landed; every wave done with this pair's blocks
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // the next pair's blocks landed (a wave with a tile waited before its
+    // stores); every wave done with this pair's blocks
+    if (jt > j_last) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     if (p.log != nullptr && lane == 0 && rg == 0 && jt <= j_last) {
       const int64_t item = ((int64_t)(tile0 + jt) * n_hg + hg) * h_kv + g;
