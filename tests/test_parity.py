@@ -8,8 +8,9 @@ import pytest
 import torch
 
 import oracle
-from parity_helpers import (TOL, binding, check_rows, check_tile_log, f64, oracle_full, oracle_rows,
-                            rel_l2, rne, row_tol_for, run_gpu, sample_rows, synth, to_device)
+from parity_helpers import (TOL, binding, check_rows, check_tile_log, f64, new_log, oracle_full,
+                            oracle_rows, rel_l2, rne, row_tol_for, run_gpu, sample_rows, synth,
+                            to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -314,5 +315,39 @@ def test_streaming_window_full_size():
         inp = synth.make(synth.ragged_bf16())
         _, _, bkv, _ = _call(inp, synth.ragged_bf16(), torch.float32)
         assert bkv == 32
+    finally:
+        binding.attn_force_config(-1)
+
+
+def test_streaming_config_falls_back_where_it_does_not_run():
+    # Forced onto calls it does not run -- full attention, a window too wide
+    # for its block ring, KV splits -- the streaming window configuration
+    # gives way to the default one: the oracle's results, and the default's
+    # 64-key tiles in the tile log.
+    try:
+        _forced("swin_r128_kv32")
+        for window in (-1, 5000):
+            case = synth.Case(f"fallback_w{window}", h_q=16, h_kv=2, d=64, sq=[200], past=[300],
+                              window=window, seed=41)
+            inp = synth.make(case)
+            out, recs, bkv, q_rows = run_gpu(to_device(inp), out_dtype=torch.float32,
+                                             log_capacity=case.tokens * case.h_q)
+            check_rows(f64(out), oracle_full(inp), case.name)
+            assert bkv == 64, case.name
+            check_tile_log(recs, bkv, q_rows, case.cu_seqlens, case.past, case.window, case.h_q)
+        case = synth.Case("fallback_split", h_q=16, h_kv=2, d=64, sq=[200], past=[300], window=128,
+                          seed=42)
+        inp = synth.make(case)
+        dev = to_device(inp)
+        out = torch.full(dev["q"].shape, float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(binding.attn_split_workspace_bytes(case.tokens, case.h_q, case.d, 2),
+                         dtype=torch.uint8, device="cuda")
+        log = new_log(2 * case.tokens * case.h_q, "cuda")
+        _, n, bkv, q_rows = binding.attn_prefill_split(
+            dev["q"], dev["k_cache"], dev["v_cache"], inp["cu_seqlens"], inp["past_len"],
+            case.window, dev["sink"], inp["scale"], out, n_split=2, workspace=ws, tile_log=log)
+        torch.cuda.synchronize()
+        check_rows(f64(out), oracle_full(inp), case.name)
+        assert bkv == 64 and n > 0
     finally:
         binding.attn_force_config(-1)
