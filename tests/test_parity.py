@@ -85,6 +85,36 @@ def test_mid_cases(spec):
     _full_check(case, every_config=True)
 
 
+def _random_cases(n=24, seed=2024):
+    """Seeded random call shapes: ragged batches (empty sequences included),
+    windows from 1 to wider than the sequence, both dtypes, d 64 and 128, and
+    group sizes that give 16-, 32- and 128-row position spans per Q tile."""
+    rng = np.random.default_rng(seed)
+    heads = [(8, 2), (16, 2), (32, 4), (8, 1), (4, 4)]
+    out = []
+    for i in range(n):
+        h_q, h_kv = heads[rng.integers(len(heads))]
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["f16", "bf16"]))
+        nb = int(rng.integers(1, 5))
+        sq = [int(rng.choice([0, 1, 7, 16, 33, 64, 100, 129, 257])) for _ in range(nb)]
+        if sum(sq) == 0:
+            sq[0] = 45
+        past = [int(rng.choice([0, 3, 31, 64, 200, 513, 1400])) for _ in range(nb)]
+        window = int(rng.choice([-1, 1, 17, 64, 100, 128, 160, 1000]))
+        out.append((f"rand{i}_{h_q}x{h_kv}_d{d}_{dtype}_w{window}", h_q, h_kv, d, sq, past, window,
+                    dtype))
+    return out
+
+
+@pytest.mark.parametrize("spec", _random_cases(), ids=lambda s: s[0])
+def test_random_shapes_every_config(spec):
+    name, h_q, h_kv, d, sq, past, window, dtype = spec
+    case = synth.Case(name, h_q=h_q, h_kv=h_kv, d=d, sq=sq, past=past, window=window, dtype=dtype,
+                      seed=500 + sum(sq) + sum(past), s_cap=max(p + s for p, s in zip(past, sq)) + 9)
+    _full_check(case, out_dtypes=("same",), every_config=True)
+
+
 def _each_config():
     """Yield every kernel configuration, forced for the calls made meanwhile
     (bitwise properties hold within one configuration; the tuner may pick
