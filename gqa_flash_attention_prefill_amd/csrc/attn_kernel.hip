@@ -214,6 +214,20 @@ __device__ inline void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_
                : "memory", "m0");
 }
 
+// The same with 4 bytes per lane (global_load_lds_dword): lane i's word
+// lands at lds_addr + 4 i.
+__device__ inline void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  sbase = reinterpret_cast<const void*>((hi << 32) | lo);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 __device__ inline uint32_t lds_byte_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -1016,9 +1030,15 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   static_assert(NS == 4 || NS == 5, "ring of 4 or 5 tiles per group");
   static_assert(NB <= 2, "one -m splat per 32-key block (negm, negm1)");
   static_assert(SLOT_CH % (64 * R) == 0, "direct loads tile a slot");
-  static_assert(2 * GROUP_CH * 16 <= 160 * 1024, "LDS");
+  static_assert(2 * GROUP_CH * 16 + (XTRA ? 2 * NS * 64 * 4 : 0) <= 160 * 1024, "LDS");
+  // the token-pool row lists run two tiles ahead of the loads that use them,
+  // which the waits below count for a 4-deep ring
+  static_assert(!XTRA || NS == 4, "split/lse variant: ring of 4 tiles per group");
 
   __shared__ u32x4 lds[2 * GROUP_CH];
+  // Token-pool layout (split/lse variant): each group's ring of the pool rows
+  // of its tiles' keys, 64 words a slot (tile j of the group in slot j % NS)
+  __shared__ int32_t kidx[XTRA ? 2 * NS * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1108,19 +1128,27 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // A group-local index past the group's last tile loads tile t_hi instead,
   // so every slot a wave reads holds finite cache data (a wave without a
   // tile still multiplies P = 0 by its V fragments).
-  // Token-pool layout: the pool row of each of this lane's keys in the next
-  // tile to load, read one tile ahead so that the index latency hides behind
-  // the phases before it (keys past the sequence read row skv - 1).
-  uint32_t prow[LPW];
+  // Token-pool layout: the pool rows of tile j's keys (keys past the sequence
+  // read row skv - 1).  Those of the prologue's tiles are read into registers
+  // at once; every later tile's 64 rows are brought into its slot of the
+  // group's LDS row ring by one 4-byte direct load per wave (each wave of the
+  // group loads the same words), issued two tiles ahead of the tile's own
+  // loads, so that the waits that land a tile also land the rows two tiles on
+  // and no load waits for a register operand still in flight.
   auto tile_key = [&](int j, int i) __attribute__((always_inline)) {
     const int t = min(t_lo + 2 * j + grp, t_hi);
     return min(t * BKV + ld_key[i], skv - 1);
   };
-  auto fetch_rows = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) prow[i] = (uint32_t)kv_list[tile_key(j, i)];
+  const uint32_t kidx_addr = lds_byte_addr(kidx) + (uint32_t)(grp * NS * 64) * 4u;
+  auto fetch_idx = [&](int j) __attribute__((always_inline)) {
+    const int t = min(t_lo + 2 * j + grp, t_hi);
+    lds_dma4(kv_list, (uint32_t)min(t * BKV + lane, skv - 1) * 4u,
+             kidx_addr + (uint32_t)((j % NS) * 64) * 4u);
   };
-  auto load_tile = [&](int j) __attribute__((always_inline)) {
+  // Token-pool layout: the pool row of this lane's piece i comes from
+  // rows[i] (the prologue's registers) or, with rows = nullptr, from the
+  // tile's slot of the LDS row ring.
+  auto load_tile = [&](int j, const uint32_t* rows) __attribute__((always_inline)) {
     const int t = min(t_lo + 2 * j + grp, t_hi);
     const uint32_t st = ring_addr + (uint32_t)((j % NS) * SLOT_CH) * 16u;
     const bool tail = t * BKV + BKV > skv;  // the tile that crosses the end of the keys
@@ -1131,7 +1159,9 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       const int blk = qi % (TILE_CH / 64);
       if (paged) {
         // pool row (clamped into the pool) + this lane's chunk of the row
-        const uint32_t r = min(prow[i], p.n_pool - 1u);
+        const uint32_t row =
+            rows ? rows[i] : (uint32_t)kidx[(grp * NS + j % NS) * 64 + ld_key[i]];
+        const uint32_t r = min(row, p.n_pool - 1u);
         lds_dma16(tt ? vptr : kptr, r * p.kv_row_bytes + ld_off[i] - (uint32_t)ld_key[i] * (D * 2),
                   st + (uint32_t)(tt * TILE_CH + blk * 64) * 16u);
         continue;
@@ -1447,11 +1477,18 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
   // still be in flight, so each load has about two phases to land.  (Issuing
   // K one tile earlier still, into the half of a slot that frees first, ran
   // slower.)
+  // Token-pool layout: M_j (j >= 0) also issues the row load of tile
+  // j + NS + 2 after the tile's loads, so a wait that lets M_j's tile stay in
+  // flight lets its row load too (the prologue's row loads precede its tiles),
+  // and the wait that lands tile j + 3 lands the rows of tile j + NS + 1,
+  // which M_{j+1} reads.
   auto wait_tiles = [&](int j) __attribute__((always_inline)) {
     const int newest = min(j < 0 ? NS - 1 : j + NS, n_stages - 1);  // last tile requested
     const int ahead = newest - (j + 3);  // tiles allowed in flight
     if (NS == 5 && ahead >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
+    else if (ahead >= 1 && paged && j >= 0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW + 1));
     else if (ahead >= 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
     else
@@ -1460,8 +1497,11 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
 
   // ---- prologue: tiles 0 .. NS-1 requested, 0 and 1 landed ----
   if (paged) {
-    // the pool rows of the first tiles are read together, then each tile is
-    // issued (one index round trip instead of one per tile)
+    // the row ring's first two tiles (NS, NS + 1) before every tile load;
+    // then the pool rows of the first tiles, read together into registers,
+    // and each tile issued (one index round trip instead of one per tile)
+    fetch_idx(NS);
+    fetch_idx(NS + 1);
     uint32_t pre[NS][LPW];
 #pragma unroll
     for (int j = 0; j < NS; ++j)
@@ -1470,15 +1510,12 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       if (j >= n_stages) break;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) prow[i] = pre[j][i];
-      load_tile(j);
+      load_tile(j, pre[j]);
     }
-    if (NS < n_stages) fetch_rows(NS);
   } else {
 #pragma unroll
     for (int j = 0; j < NS; ++j)
-      if (j < n_stages) load_tile(j);
+      if (j < n_stages) load_tile(j, nullptr);
   }
   prepare_q<TI, KSTEPS>(qf, c, valid);
   {
@@ -1526,14 +1563,16 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
     // the direct loads go after the MFMAs: issued while the last ones drain
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFast) {
-      if (paged)
-        load_tile(j + NS);
-      else
+      if (paged) {
+        load_tile(j + NS, nullptr);
+        fetch_idx(j + NS + 2);
+      } else {
         load_inner_tile(j + NS);
+      }
     } else if (j >= 0 && j + NS < n_stages) {
-      load_tile(j + NS);
+      load_tile(j + NS, nullptr);
+      if (paged) fetch_idx(j + NS + 2);
     }
-    if (paged && j >= 0 && j + NS + 1 < n_stages) fetch_rows(j + NS + 1);
     __builtin_amdgcn_s_setprio(0);
     barrier();
     // ---- V_j ----
@@ -1541,10 +1580,10 @@ __global__ __launch_bounds__(512) void attn_pp_kernel(Params p) {
       v_fast(j);
       if constexpr (NS >= 5)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
-      else if constexpr (NS == 4)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+      else if (paged)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW + 1));
       else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
     } else {
       v_phase(j);
       wait_tiles(j);

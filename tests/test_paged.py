@@ -27,6 +27,13 @@ CASES = [
     synth.Case("p_bf16_d128", h_q=16, h_kv=2, d=128, sq=[150, 64], past=[300, 1000], window=128,
                dtype="bf16", seed=63),
     synth.Case("p_d256", h_q=4, h_kv=2, d=256, sq=[90], past=[200], window=-1, seed=64),
+    # long sequences: dozens of KV tiles per Q tile, so the pool-row lists of
+    # the ping-pong kernel cycle through their ring many times, and Q tiles of
+    # one call span 1 .. 80 tiles (every prologue / steady / tail transition)
+    synth.Case("p_long", h_q=16, h_kv=2, d=64, sq=[512, 37, 200], past=[3000, 5000, 0],
+               window=-1, seed=71),
+    synth.Case("p_long_w_bf16", h_q=16, h_kv=2, d=64, sq=[300], past=[6000], window=1000,
+               dtype="bf16", seed=72),
 ]
 
 
