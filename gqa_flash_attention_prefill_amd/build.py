@@ -72,5 +72,37 @@ def build(verbose: bool = False, extra_flags=None, out=None, jobs=None) -> str:
     return out
 
 
+# AddressSanitizer + UBSan on the host side of the C ABI layer only (each
+# -fsanitize after -Xarch_host: device code is never built with them), linked
+# with the device objects of the last build() into a separate library that
+# only the host-sanitizer test loads, under the clang ASan runtime.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+LIB_HOST_SANITIZED = os.path.join(OBJ, "libattn_prefill_host_sanitized.so")
+
+
+def build_host_sanitized() -> str:
+    """Link LIB_HOST_SANITIZED from a host-sanitized compile of the C ABI
+    layer and the kernel objects of the last build() (which must exist)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    kernels = [os.path.join(OBJ, f"libattn_prefill_cfg{i}.o") for i in range(N_CONFIGS)]
+    kernels.append(os.path.join(OBJ, "libattn_prefill_table.o"))
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        raise RuntimeError(f"kernel objects missing ({missing[0]}): run build() first")
+    api_o = os.path.join(OBJ, "host_sanitized_api.o")
+    rc, err = _run([hipcc] + HIPCC_FLAGS + HOST_SANITIZE + ["-c", API, "-o", api_o])
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed on the sanitized C ABI layer ({rc}):\n{err}")
+    out = LIB_HOST_SANITIZED
+    rc, err = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + HOST_SANITIZE +
+                   kernels + [api_o, "-o", out + ".tmp"])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
