@@ -170,3 +170,31 @@ def test_noncausal_pool_call():
                                out, causal=False)
     torch.cuda.synchronize()
     assert rel_l2(f64(out), ref) <= TOL
+
+
+def _random_pool_cases(n=12, seed=3031):
+    """Seeded random ragged batches for the token-pool layout: long prefixes
+    (so the ping-pong kernel's LDS row ring wraps many times), empty and
+    one-row sequences, windows from none to wider than the sequence, both
+    dtypes, d 64 and 128."""
+    rng = np.random.default_rng(seed)
+    heads = [(8, 2), (16, 2), (64, 8), (8, 1)]
+    out = []
+    for i in range(n):
+        h_q, h_kv = heads[rng.integers(len(heads))]
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["f16", "bf16"]))
+        nb = int(rng.integers(1, 4))
+        sq = [int(rng.choice([0, 1, 16, 77, 130, 300])) for _ in range(nb)]
+        if sum(sq) == 0:
+            sq[0] = 50
+        past = [int(rng.choice([0, 63, 700, 2100, 4100])) for _ in range(nb)]
+        window = int(rng.choice([-1, -1, 1, 128, 1000]))
+        out.append(synth.Case(f"prand{i}_{h_q}x{h_kv}_d{d}_{dtype}_w{window}", h_q=h_q, h_kv=h_kv,
+                              d=d, sq=sq, past=past, window=window, dtype=dtype, seed=900 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_pool_cases(), ids=lambda c: c.name)
+def test_random_pool_shapes_every_config(case):
+    test_pool_equals_dense_bitwise_and_matches_oracle(case)
