@@ -36,11 +36,14 @@
 //     costs ~1e-3 relative error.
 //   * Two waves per row group (KV splits) take alternate tiles, so each
 //     SIMD holds two independent waves; their partial (m, l, O) are merged
-//     through LDS before the epilogue.  Two kernels share all of the above:
-//     attn_fwd_kernel, where each wave software-pipelines the matrix work of
-//     one tile with the vector work of the previous one, and attn_pp_kernel
-//     (d 64), where the two waves of a SIMD alternate whole matrix and
-//     vector phases between workgroup barriers.
+//     through LDS before the epilogue.  Three kernels share all of the
+//     above: attn_fwd_kernel, where each wave software-pipelines the matrix
+//     work of one tile with the vector work of the previous one;
+//     attn_pp_kernel (d 64), where the two waves of a SIMD alternate whole
+//     matrix and vector phases between workgroup barriers; and
+//     attn_swin_kernel (window calls of long chunks), where one workgroup
+//     walks a run of consecutive Q tiles whose windows share an LDS ring of
+//     32-key blocks.
 //
 // KV loop bounds ("window in v5"; sglang 34468 "bound the stage-1 prefix
 // loop"): the loop starts at the tile holding the lowest key the Q tile's
