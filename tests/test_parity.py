@@ -381,3 +381,14 @@ def test_streaming_config_falls_back_where_it_does_not_run():
         assert bkv == 64 and n > 0
     finally:
         binding.attn_force_config(-1)
+
+
+@pytest.mark.parametrize("dtype,window", [("f16", -1), ("bf16", 4096)])
+def test_long_context_128k_keys(dtype, window):
+    # A 256-row chunk after 130,816 cached keys (131,072 in all): thousands of
+    # KV tiles per Q tile (the ping-pong kernel's steady loop, the lazy
+    # rescale and fp32 accumulation over 128k keys), whole outputs against the
+    # oracle and tile logs, on every configuration.
+    case = synth.Case(f"ctx128k_{dtype}_w{window}", h_q=8, h_kv=1, d=64, sq=[256], past=[130816],
+                      window=window, dtype=dtype, seed=51)
+    _full_check(case, every_config=True)
