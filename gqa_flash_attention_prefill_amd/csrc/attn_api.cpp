@@ -266,11 +266,8 @@ int sweep(const Call& c_in, int* best_out) {
   // back to back until at least kMinBatchUs of work is timed, and it is
   // ranked by the median of its three per-call times.  Short calls (window
   // chunks, decode rows) then get tens of repetitions per pass, and one slow
-  // or fast outlier pass does not decide the choice.  The window-chunk
-  // configurations lie within 1-2 % of each other when one call is repeated
-  // (its Q chunk stays in cache), so the batch is long enough (about 60
-  // launches of such a call) to resolve that.
-  constexpr float kMinBatchUs = 500.f;
+  // or fast outlier pass does not decide the choice.
+  constexpr float kMinBatchUs = 150.f;
   constexpr int kPasses = 3;
   const int n_cfg = attn::config_count();
   std::vector<float> pass_us(n_cfg * kPasses, INFINITY);

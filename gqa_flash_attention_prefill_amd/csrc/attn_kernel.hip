@@ -379,21 +379,39 @@ __device__ __attribute__((always_inline)) void finish_row(const Params& p, const
   if (any) l_tot += __builtin_amdgcn_exp2f(sink * kLog2e - m_run);  // exp2(-inf) = 0: no sink
   const float inv = 1.f / fmaxf(l_tot, FLT_MIN);
   const int64_t ooff = row * D;
+  if constexpr (sizeof(TO) == 4) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = db * 32 + i4 * 8 + half * 4;
-      const float o0 = acc[db][i4 * 4 + 0] * inv, o1 = acc[db][i4 * 4 + 1] * inv;
-      const float o2 = acc[db][i4 * 4 + 2] * inv, o3 = acc[db][i4 * 4 + 3] * inv;
-      if constexpr (sizeof(TO) == 4) {
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = db * 32 + i4 * 8 + half * 4;
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + ooff + d0) =
-            f32x4{o0, o1, o2, o3};
-      } else {
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
-            u32x2{TI::pack(o0, o1), TI::pack(o2, o3)};
+            f32x4{acc[db][i4 * 4 + 0] * inv, acc[db][i4 * 4 + 1] * inv,
+                  acc[db][i4 * 4 + 2] * inv, acc[db][i4 * 4 + 3] * inv};
       }
-    }
+  } else {
+    // In each 16-value run of d (db, k) the low lanes hold values 0-3 and
+    // 8-11, the high lanes (same row) 4-7 and 12-15.  One v_permlane32_swap
+    // per register gives the low lanes 8-15 and the high lanes 0-7, so each
+    // lane stores 16 contiguous bytes: half as many store instructions, each
+    // writing 32 contiguous bytes of every row it touches.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i0 = 8 * k, i1 = 8 * k + 4;
+        const uint32_t w0a = TI::pack(acc[db][i0 + 0] * inv, acc[db][i0 + 1] * inv);
+        const uint32_t w0b = TI::pack(acc[db][i0 + 2] * inv, acc[db][i0 + 3] * inv);
+        const uint32_t w1a = TI::pack(acc[db][i1 + 0] * inv, acc[db][i1 + 1] * inv);
+        const uint32_t w1b = TI::pack(acc[db][i1 + 2] * inv, acc[db][i1 + 3] * inv);
+        // swap(x, y): x's high lanes <-> y's low lanes
+        const auto sa = __builtin_amdgcn_permlane32_swap(w1a, w0a, false, false);
+        const auto sb = __builtin_amdgcn_permlane32_swap(w1b, w0b, false, false);
+        const int d0 = db * 32 + 16 * k + (half ? 0 : 8);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + ooff + d0) =
+            u32x4{sa[0], sb[0], sa[1], sb[1]};
+      }
+  }
   if (XTRA && p.lse != nullptr && half == 0)
     p.lse[row] = any ? (m_run + __builtin_amdgcn_logf(l_kept)) * kLn2 : kNegInf;
 }

@@ -281,7 +281,7 @@ const char* attn_last_error(void);
  * tokens of the call, h_q, group size, window, batch).  The first call for a
  * key times every kernel configuration (a synchronous sweep on the caller's
  * stream, without the sink: three interleaved passes, each timing a
- * configuration over at least ~500 us of back-to-back launches, ranked by
+ * configuration over at least ~150 us of back-to-back launches, ranked by
  * the median) and keeps the fastest; later calls with the same key reuse
  * it.  Since the key leaves out the KV depth, the sweep
  * times every sequence at depth max(past_len, min(s_cap, 16384) - sq) of the

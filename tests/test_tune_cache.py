@@ -39,7 +39,7 @@ def test_one_sweep_per_layer_type_over_a_chunked_prefill(monkeypatch):
     assert st["cached_keys"] == 2, st
     # each sweep times every configuration in three passes: a warm-up, a
     # first batch of three launches, a longer batch (at most 64) when three
-    # take under ~500 us, and two more passes of the same length
+    # take under ~150 us, and two more passes of the same length
     assert 2 * n_cfg * 10 <= st["tuning_launches"] <= 2 * n_cfg * (1 + 3 + 3 * 64), st
     for _, _, out in layers:
         assert torch.isfinite(out).all()
